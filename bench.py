@@ -1,0 +1,263 @@
+"""Benchmark of the block-wise FP8 ZeRO-1 shard step on one MI355X.
+
+One step = the whole per-step path of one rank: fold its row-major FP32
+grads into the tile-major shard (pack_shard), the fused AdamW + per-tile
+E4M3 requantization (adamw_fp8_step), and the unfold of codes and scales
+into row-major FP8 weights plus the scale grid (unpack_fp8).  The split
+itself (the planner) runs once at set-up.
+
+Default workload: the dense-LLM rank shard -- 32 layers x {4 of 4096x4096,
+2 of 4096x11008, 1 of 11008x4096}, D = 8, rank 0: 49408 tiles, 809.5M
+elements.  Its moments are warm from 10 prior steps (t = 1..10, fresh
+N(0, 1e-3) grads each); the timed steps continue at t = 11, 12, ... on the
+t = 11 gradients, which stay resident in HBM (inputs are never re-drawn
+inside the timed region).
+
+Output: one JSON line.  value = shard elements per second of the whole
+step.  roofline = the fused step kernel's algorithmic HBM bytes per launch
+(29 B per element + 4 B per tile) over its mean launch time, measured with
+HIP events on the stream the kernels run on.  cpu_baseline = the C oracle
+on a bounded sample of the same workload, on the host's cores.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "AdamW+blockwise-FP8 requant elems/s and HBM GB/s (% of peak) on one MI355X"
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published peak
+STEP_BYTES_PER_ELEM = 29          # read p, g, m, v (16) + write p, m, v (12) + code (1)
+STEP_BYTES_PER_TILE = 4           # scale_inv
+PACK_BYTES_PER_ELEM = 8           # read grad + write tile
+UNPACK_BYTES_PER_ELEM = 2         # read code + write code
+UNPACK_BYTES_PER_TILE = 8         # read + write scale
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "step_kernel_dense_llm_traffic.md")
+KERNEL_SRC = os.path.join(ROOT, "blockwise_fp8_zero_amd", "csrc", "kernels.hip")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(per_launch_algo_bytes):
+    """HBM bytes per launch of the step kernel from the committed rocprofv3
+    PMC summary, if it was taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    sha = re.search(r"kernel_sha256:\s*([0-9a-f]{64})", text)
+    tb = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not sha or not tb or sha.group(1) != kernel_sha():
+        return None
+    return float(tb.group(1))
+
+
+def cpu_baseline(w, target_s=10.0):
+    """The C oracle (fold of the grads, AdamW + requant, unfold) on a slab of
+    the workload's first weight, 1024 x 4096 (256 tiles), stepped repeatedly
+    by every host thread for about target_s seconds."""
+    import ctypes as C
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+    import synth
+    from synth import workloads as WL
+
+    threads = min(16, os.cpu_count() or 1)
+    E, H, W = 1, 1024, w.dims[0][2]
+    dims = np.array([[E, H, W]], dtype=np.int64)
+    q, owned, table = oracle.plan(dims, 1, 0)
+    n = q * oracle.TILE_ELEMS
+    master_rm = synth.fill_rect_host(w.recipe(WL.MASTER, 0), 0, 0, H, 0, W)
+    grad_rm = synth.fill_rect_host(w.recipe(WL.GRAD, 0, w.measured_step), 0, 0, H, 0, W)
+    L = oracle.lib()
+    hp = oracle.hparams(step=w.measured_step, **WL.HP)
+    P = C.c_void_p
+
+    def ptr(a):
+        return a.ctypes.data_as(P)
+
+    def one_pass(state):
+        g_tiles, p, m, v, codes, sc, out8, outsc = state
+        srcs = (P * 1)(grad_rm.ctypes.data)
+        L.ora_pack(ptr(dims), 1, C.cast(srcs, P), ptr(table), q, ptr(g_tiles))
+        L.ora_step(ptr(p), ptr(g_tiles), ptr(m), ptr(v), q, C.byref(hp), ptr(codes), ptr(sc),
+                   None, 1e-6)
+        d8 = (P * 1)(out8.ctypes.data)
+        ds = (P * 1)(outsc.ctypes.data)
+        L.ora_unpack(ptr(dims), 1, ptr(codes), ptr(sc), ptr(table), q, C.cast(d8, P), C.cast(ds, P))
+
+    def new_state():
+        srcs = [np.ascontiguousarray(master_rm.reshape(E, H, W))]
+        p = oracle.pack(dims, srcs, table)
+        return [np.empty(n, np.float32), p, np.zeros(n, np.float32), np.zeros(n, np.float32),
+                np.empty(n, np.uint8), np.empty(q, np.float32), np.empty(E * H * W, np.uint8),
+                np.empty(q, np.float32)]
+
+    # calibrate the number of passes on one thread
+    st = new_state()
+    t0 = time.perf_counter()
+    one_pass(st)
+    per_pass = time.perf_counter() - t0
+    passes = max(1, int(round(target_s / per_pass)))
+    states = [new_state() for _ in range(threads)]
+
+    def work(k):
+        for _ in range(passes):
+            one_pass(states[k])
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(work, range(threads)))
+    dt = time.perf_counter() - t0
+    elems = threads * passes * n
+    return {"value": elems / dt, "unit": "elem/s", "cores": threads, "kind": "oracle",
+            "sample": f"fold + AdamW/E4M3 step + unfold of a {H}x{W} slab (256 tiles, "
+                      f"{n / 1e6:.1f}M elements) of the first dense-LLM weight at t="
+                      f"{w.measured_step}, {passes} passes on each of {threads} threads, "
+                      f"{dt:.1f} s wall",
+            "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dense_llm",
+                    choices=["dense_llm", "ragged", "moe_experts", "large", "tiny"])
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import blockwise_fp8_zero_amd as bfz
+    from synth import workloads as WL
+    from tests.gpu_run import GpuWorkload
+
+    torch.cuda.set_device(0)
+    w = WL.BY_NAME[args.workload]()
+    log(f"workload {w.name}: {w.description}")
+    t0 = time.perf_counter()
+    g = GpuWorkload(w)
+    g.load_state()
+    prior = w.steps[:-1]
+    if prior:
+        g.run_steps(prior)
+    g.draw_grads(w.measured_step)
+    fp8, sc = g.alloc_rowmajor_out()
+    # a plain 1 GiB device copy, outside the timed region: the reference
+    # kernel of known size for scaling the HBM byte counters
+    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    del a, b
+    torch.cuda.synchronize()
+    log(f"set-up {time.perf_counter() - t0:.1f} s; q={g.q} tiles, owned={g.owned}")
+
+    stream = torch.cuda.current_stream()
+    t_next = w.measured_step
+
+    def one_step(t, ev=None):
+        g.pack_grads()
+        if ev is not None:
+            ev[0].record(stream)
+        g.step(t)
+        if ev is not None:
+            ev[1].record(stream)
+        g.unpack(fp8, sc)
+
+    for _ in range(args.warmup):
+        one_step(t_next)
+        t_next += 1
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(args.steps):
+        one_step(t_next, evs[k])
+        t_next += 1
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    step_kernel_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps
+    ms_per_step = total_ms / args.steps
+
+    elems = g.q * bfz.TILE_ELEMS
+    valid = sum(min(128, int(r[4])) * min(128, int(r[5])) for r in g.table[:g.owned]) \
+        if w.name == "ragged" else g.owned * bfz.TILE_ELEMS
+    algo_bytes = STEP_BYTES_PER_ELEM * elems + STEP_BYTES_PER_TILE * g.q
+    achieved = algo_bytes / (step_kernel_ms * 1e-3) / 1e9
+    whole_bytes = algo_bytes + PACK_BYTES_PER_ELEM * elems + \
+        UNPACK_BYTES_PER_ELEM * elems + UNPACK_BYTES_PER_TILE * g.q
+    traffic = measured_traffic(algo_bytes) if w.name == "dense_llm" else None
+
+    out = {
+        "metric": METRIC,
+        "value": elems / (ms_per_step * 1e-3),
+        "unit": "elem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {w.description}",
+            "shard_tiles": g.q,
+            "shard_elems": elems,
+            "valid_elems": valid,
+            "D": w.D,
+            "rank": w.rank,
+            "first_timed_step_t": w.measured_step + args.warmup,
+            "step_path": "pack_shard(grad) + adamw_fp8_step + unpack_fp8",
+        },
+        "step_hbm_GBps": whole_bytes / (ms_per_step * 1e-3) / 1e9,
+        "step_hbm_frac": whole_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "adamw_fp8_step_ms": step_kernel_ms,
+        "adamw_fp8_step_elems_per_s": elems / (step_kernel_ms * 1e-3),
+        "roofline": {
+            "kernel": "adamw_fp8_step (step_kernel)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": algo_bytes,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.skip_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

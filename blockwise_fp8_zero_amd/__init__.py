@@ -1,0 +1,199 @@
+"""Python binding of libbfz.so, the block-wise FP8 ZeRO-1 shard step.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels (see include/bfz.h for the operations, layouts and error codes).
+PyTorch supplies device memory and the stream; the functions take torch
+tensors, check dtype / device / size, and pass raw pointers plus
+torch.cuda.current_stream() to the C ABI.  If the library is not built,
+importing works but every call raises -- there is no fallback path.
+"""
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbfz.so")
+TILE = 128
+TILE_ELEMS = TILE * TILE
+
+BFZ_OK, BFZ_EINVAL, BFZ_EALIGN, BFZ_EHIP, BFZ_ESTATE = 0, -1, -2, -3, -4
+
+
+class BfzError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"bfz error {code}: {msg}")
+        self.code = code
+
+
+class AdamW(C.Structure):
+    """Hyper-parameters of one step; step is the counter t >= 1."""
+    _fields_ = [("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
+                ("eps", C.c_double), ("weight_decay", C.c_double), ("step", C.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libbfz.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built (run __graft_entry__.build()); "
+                               "this package has no non-HIP fallback")
+        L = C.CDLL(LIB_PATH)
+        P, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
+        L.bfz_plan_create.argtypes = [P, i32, i32, i32, C.POINTER(P)]
+        L.bfz_plan_upload.argtypes = [P]
+        L.bfz_plan_destroy.argtypes = [P]
+        L.bfz_plan_destroy.restype = None
+        for n in ("bfz_plan_shard_tiles", "bfz_plan_owned_tiles", "bfz_plan_total_tiles"):
+            getattr(L, n).argtypes = [P]
+            getattr(L, n).restype = i64
+        L.bfz_plan_table.argtypes = [P, P]
+        L.bfz_plan_tile.argtypes = [P, i64, P]
+        L.pack_shard.argtypes = [P, P, P, P]
+        L.adamw_fp8_step.argtypes = [P, P, P, P, P, P, i64, C.POINTER(AdamW), P]
+        L.unpack_fp8.argtypes = [P, P, P, P, P, P]
+        L.bfz_e4m3_encode.argtypes = [P, P, i64, P]
+        L.bfz_last_error.argtypes = []
+        L.bfz_last_error.restype = C.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != BFZ_OK:
+        raise BfzError(rc, lib().bfz_last_error().decode())
+    return rc
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _dev(t, dtype, name, numel=None):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise TypeError(f"{name}: need a contiguous {dtype} CUDA tensor")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: needs at least {numel} elements, has {t.numel()}")
+    return C.c_void_p(t.data_ptr())
+
+
+class Plan:
+    """Rank `rank`'s block-wise split of the weights `dims` over D ranks.
+
+    dims: sequence of (E, H, W) (E experts of H x W; E = 1 for a matrix).
+    upload=True copies the tile table to the current device (needed before
+    pack_shard / unpack_fp8); the planner itself runs on the host.
+    """
+
+    def __init__(self, dims, D=1, rank=0, upload=True):
+        self.dims = [tuple(int(x) for x in d) for d in dims]
+        arr = (C.c_int64 * (3 * max(1, len(self.dims))))(*[x for d in self.dims for x in d])
+        h = C.c_void_p()
+        _check(lib().bfz_plan_create(C.cast(arr, C.c_void_p), len(self.dims), D, rank, C.byref(h)))
+        self._h = h
+        self.D, self.rank = D, rank
+        if upload:
+            self.upload()
+
+    def upload(self):
+        _check(lib().bfz_plan_upload(self._h))
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def shard_tiles(self):
+        return int(lib().bfz_plan_shard_tiles(self._h))
+
+    @property
+    def owned_tiles(self):
+        return int(lib().bfz_plan_owned_tiles(self._h))
+
+    @property
+    def total_tiles(self):
+        return int(lib().bfz_plan_total_tiles(self._h))
+
+    def table(self):
+        """numpy int64 [q, 6]: weight, expert, tile row, tile col, valid rows, valid cols."""
+        import numpy as np
+        out = np.empty((self.shard_tiles, 6), dtype=np.int64)
+        _check(lib().bfz_plan_table(self._h, out.ctypes.data_as(C.c_void_p)))
+        return out
+
+    def tile(self, slot):
+        out = (C.c_int64 * 6)()
+        _check(lib().bfz_plan_tile(self._h, slot, C.cast(out, C.c_void_p)))
+        return tuple(out)
+
+    def close(self):
+        if self._h:
+            lib().bfz_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _ptr_array(tensors, dtype, name, n):
+    arr = (C.c_void_p * max(1, n))()
+    for k in range(n):
+        t = tensors[k] if k < len(tensors) else None
+        if t is not None:
+            arr[k] = _dev(t, dtype, f"{name}[{k}]").value
+    return arr
+
+
+def pack_shard(plan: Plan, srcs, dst, stream=None):
+    """Fold the weights' row-major FP32 tensors (srcs[p], or None for weights
+    the rank does not touch) into the tile-major shard dst (q * 16384 floats)."""
+    import torch
+    arr = _ptr_array(srcs, torch.float32, "srcs", len(plan.dims))
+    d = _dev(dst, torch.float32, "dst", plan.shard_tiles * TILE_ELEMS)
+    _check(lib().pack_shard(plan.handle, C.cast(arr, C.c_void_p), d, _stream(stream)))
+
+
+def adamw_fp8_step(master, grad, m, v, codes, scale_inv, hp, n_tiles=None, stream=None):
+    """Fused AdamW + per-tile E4M3 requant over n_tiles whole tiles (default:
+    all of master).  hp: AdamW, or a dict of its fields."""
+    import torch
+    if isinstance(hp, dict):
+        hp = AdamW(**hp)
+    if n_tiles is None:
+        if master.numel() % TILE_ELEMS:
+            raise ValueError("master is not a whole number of tiles")
+        n_tiles = master.numel() // TILE_ELEMS
+    n = n_tiles * TILE_ELEMS
+    args = [_dev(master, torch.float32, "master", n), _dev(grad, torch.float32, "grad", n),
+            _dev(m, torch.float32, "m", n), _dev(v, torch.float32, "v", n),
+            _dev(codes, torch.uint8, "codes", n), _dev(scale_inv, torch.float32, "scale_inv", n_tiles)]
+    _check(lib().adamw_fp8_step(*args, n_tiles, C.byref(hp), _stream(stream)))
+
+
+def unpack_fp8(plan: Plan, codes, scale_inv, dst_fp8, dst_scale, stream=None):
+    """Unfold the shard's codes and scales into row-major uint8 weights
+    dst_fp8[p] (E, H, W) and scale grids dst_scale[p] (E, ceil(H/128), ceil(W/128))."""
+    import torch
+    n = len(plan.dims)
+    a8 = _ptr_array(dst_fp8, torch.uint8, "dst_fp8", n)
+    asc = _ptr_array(dst_scale, torch.float32, "dst_scale", n)
+    q = plan.shard_tiles
+    _check(lib().unpack_fp8(plan.handle, _dev(codes, torch.uint8, "codes", q * TILE_ELEMS),
+                            _dev(scale_inv, torch.float32, "scale_inv", q),
+                            C.cast(a8, C.c_void_p), C.cast(asc, C.c_void_p), _stream(stream)))
+
+
+def e4m3_encode(x, out, stream=None):
+    """out[k] = E4M3 code of x[k] (the step kernel's rounding), device tensors."""
+    import torch
+    n = x.numel()
+    _check(lib().bfz_e4m3_encode(_dev(x, torch.float32, "x"), _dev(out, torch.uint8, "out", n), n,
+                                 _stream(stream)))

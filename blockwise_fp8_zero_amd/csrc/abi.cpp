@@ -1,0 +1,137 @@
+// The C ABI: argument checks, per-step scalars, launches, error strings.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "bfz_internal.h"
+
+namespace bfz {
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int hip_fail(const char* where, int err) {
+    return fail(BFZ_EHIP, "%s: %s", where, hip_error_string(err));
+}
+
+// Owned slots reference only weights whose pointer must then be non-null.
+int check_weights(const bfz_plan* plan, const void* const* ptrs, const char* where) {
+    for (const Segment& seg : plan->segments)
+        for (int32_t w = seg.weight0; w < seg.weight0 + seg.n_weights; ++w)
+            if (!ptrs[w])
+                return fail(BFZ_EINVAL, "%s: pointer of weight %d is NULL but the rank owns its tiles",
+                            where, w);
+    return BFZ_OK;
+}
+
+}  // namespace
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+}  // namespace bfz
+
+using namespace bfz;
+
+extern "C" const char* bfz_last_error(void) { return g_last_error; }
+
+extern "C" int pack_shard(const bfz_plan* plan, const float* const* src, float* dst, void* stream) {
+    if (!plan || !src || !dst) return fail(BFZ_EINVAL, "pack_shard: null pointer");
+    if (!plan->d_entries) return fail(BFZ_ESTATE, "pack_shard: plan not uploaded (bfz_plan_upload)");
+    if (!aligned(dst, 16)) return fail(BFZ_EALIGN, "pack_shard: dst must be 16-byte aligned");
+    int rc = check_weights(plan, reinterpret_cast<const void* const*>(src), "pack_shard");
+    if (rc) return rc;
+    for (int32_t w = 0; w < plan->n_weights; ++w)
+        if (src[w] && !aligned(src[w], 4))
+            return fail(BFZ_EALIGN, "pack_shard: weight %d must be 4-byte aligned", w);
+    for (const Segment& seg : plan->segments) {
+        PackArgs args{};
+        for (int32_t k = 0; k < seg.n_weights; ++k) args.src[k] = src[seg.weight0 + k];
+        int err = launch_pack(plan->d_entries + seg.slot0, seg.n_slots,
+                              dst + seg.slot0 * kTileElems, args, stream);
+        if (err != hipSuccess) return hip_fail("pack_shard", err);
+    }
+    return BFZ_OK;
+}
+
+extern "C" int unpack_fp8(const bfz_plan* plan, const uint8_t* codes, const float* scale_inv,
+                          uint8_t* const* dst_fp8, float* const* dst_scale, void* stream) {
+    if (!plan || !codes || !scale_inv || !dst_fp8 || !dst_scale)
+        return fail(BFZ_EINVAL, "unpack_fp8: null pointer");
+    if (!plan->d_entries) return fail(BFZ_ESTATE, "unpack_fp8: plan not uploaded (bfz_plan_upload)");
+    if (!aligned(codes, 16)) return fail(BFZ_EALIGN, "unpack_fp8: codes must be 16-byte aligned");
+    if (!aligned(scale_inv, 4)) return fail(BFZ_EALIGN, "unpack_fp8: scale_inv must be 4-byte aligned");
+    int rc = check_weights(plan, reinterpret_cast<const void* const*>(dst_fp8), "unpack_fp8");
+    if (rc) return rc;
+    rc = check_weights(plan, reinterpret_cast<const void* const*>(dst_scale), "unpack_fp8 (scale)");
+    if (rc) return rc;
+    for (int32_t w = 0; w < plan->n_weights; ++w)
+        if (dst_scale[w] && !aligned(dst_scale[w], 4))
+            return fail(BFZ_EALIGN, "unpack_fp8: scale grid %d must be 4-byte aligned", w);
+    for (const Segment& seg : plan->segments) {
+        if (seg.n_weights == 0) continue;  // padding slots carry nothing back
+        UnpackArgs args{};
+        for (int32_t k = 0; k < seg.n_weights; ++k) {
+            args.codes[k] = dst_fp8[seg.weight0 + k];
+            args.scale[k] = dst_scale[seg.weight0 + k];
+        }
+        int err = launch_unpack(plan->d_entries + seg.slot0, seg.n_slots,
+                                codes + seg.slot0 * kTileElems, scale_inv + seg.slot0, args, stream);
+        if (err != hipSuccess) return hip_fail("unpack_fp8", err);
+    }
+    return BFZ_OK;
+}
+
+extern "C" int adamw_fp8_step(float* master, const float* grad, float* m, float* v,
+                              uint8_t* codes, float* scale_inv, int64_t n_tiles,
+                              const bfz_adamw* hp, void* stream) {
+    if (!master || !grad || !m || !v || !codes || !scale_inv || !hp)
+        return fail(BFZ_EINVAL, "adamw_fp8_step: null pointer");
+    if (n_tiles < 0 || n_tiles > 0x7FFFFFFF)
+        return fail(BFZ_EINVAL, "adamw_fp8_step: n_tiles %lld outside [0, 2^31)", (long long)n_tiles);
+    if (!aligned(master, 16) || !aligned(grad, 16) || !aligned(m, 16) || !aligned(v, 16) ||
+        !aligned(codes, 16))
+        return fail(BFZ_EALIGN, "adamw_fp8_step: master, grad, m, v and codes must be 16-byte aligned");
+    if (!aligned(scale_inv, 4)) return fail(BFZ_EALIGN, "adamw_fp8_step: scale_inv must be 4-byte aligned");
+    const double lr = hp->lr, b1 = hp->beta1, b2 = hp->beta2, eps = hp->eps, wd = hp->weight_decay;
+    if (!std::isfinite(lr) || !std::isfinite(eps) || !std::isfinite(wd) || !(eps >= 0.0) ||
+        !(b1 >= 0.0 && b1 < 1.0) || !(b2 >= 0.0 && b2 < 1.0) || hp->step < 1)
+        return fail(BFZ_EINVAL,
+                    "adamw_fp8_step: need finite lr/eps/weight_decay, eps >= 0, 0 <= beta < 1, step >= 1");
+    // The step's scalars, formed in double and rounded to binary32 once
+    // each: the bias corrections 1 - beta^t enter as lr / (1 - beta1^t)
+    // and sqrt(1 - beta2^t), as in the Int8AdamW step (lpnh.cn essay,
+    // section 4.3).
+    const double t = double(hp->step);
+    StepScalars s;
+    s.b1 = float(b1);
+    s.c1 = float(1.0 - b1);
+    s.b2 = float(b2);
+    s.c2 = float(1.0 - b2);
+    s.step_size = float(lr / (1.0 - std::pow(b1, t)));
+    s.sbc2 = float(std::sqrt(1.0 - std::pow(b2, t)));
+    s.eps = float(eps);
+    s.decay = float(lr * wd);
+    s.has_decay = wd != 0.0;
+    int err = launch_step(master, grad, m, v, codes, scale_inv, n_tiles, s, stream);
+    if (err != hipSuccess) return hip_fail("adamw_fp8_step", err);
+    return BFZ_OK;
+}
+
+extern "C" int bfz_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream) {
+    if (!in || !out) return fail(BFZ_EINVAL, "bfz_e4m3_encode: null pointer");
+    if (n < 0) return fail(BFZ_EINVAL, "bfz_e4m3_encode: n < 0");
+    int err = launch_encode(in, out, n, stream);
+    if (err != hipSuccess) return hip_fail("bfz_e4m3_encode", err);
+    return BFZ_OK;
+}

@@ -1,0 +1,261 @@
+// CDNA4 (gfx950) kernels of the shard step: fold, fused AdamW + E4M3
+// requantization, unfold.  All three are HBM-streaming kernels -- no
+// contraction, so no MFMA -- built around one 128x128 tile per workgroup.
+//
+// Floating point: every element operation is one IEEE binary32 operation
+// in the order the update defines (no contraction into FMA: the file
+// pragma and -ffp-contract=off; sqrtf and '/' are the correctly rounded
+// HIP defaults), so results do not depend on instruction scheduling.
+#include <hip/hip_runtime.h>
+
+#include "bfz_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace bfz {
+namespace {
+
+constexpr int kThreads = 256;                            // 4 wave64s per tile
+constexpr int kWaves = kThreads / 64;
+constexpr int kStepVec = kTileElems / 4 / kThreads;      // float4 per thread per array
+
+// ---------------------------------------------------------------------
+// E4M3 (OCP E4M3FN) rounding of a binary32 value: nearest value, ties to
+// even, saturating at +-448, sign kept.  Pure integer work on the bits.
+// Normal range (|y| >= 2^-6): drop 20 mantissa bits with round-half-even
+// (the carry may step into the exponent, which is the right answer), then
+// re-bias the exponent from 127 to 7.  Below 2^-6 the E4M3 values are the
+// multiples of 2^-9, so the code is |y| * 2^9 rounded half-even (exact
+// scaling; 8 rounds up into the smallest normal, code 0x08, correctly).
+// ---------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+    const uint32_t bits = __float_as_uint(y);
+    const uint32_t sign = (bits >> 24) & 0x80u;
+    const uint32_t mag = bits & 0x7FFFFFFFu;
+    uint32_t code;
+    if (mag >= 0x43E00000u) {                 // |y| >= 448 (and Inf): saturate
+        code = 0x7Eu;
+    } else if (mag >= 0x3C800000u) {          // 2^-6 <= |y| < 448
+        const uint32_t r = mag + 0x7FFFFu + ((mag >> 20) & 1u);
+        code = (r >> 20) - ((127u - 7u) << 3);
+    } else {                                  // |y| < 2^-6
+        code = (uint32_t)__builtin_rintf(__uint_as_float(mag) * 512.0f);
+    }
+    return code | sign;
+}
+
+// AdamW of one element, the update of the Int8AdamW step (lpnh.cn essay,
+// section 4.3): moments, bias-corrected denominator, step, then decay of
+// the updated value.
+__device__ __forceinline__ void adamw_elem(float& p, float g, float& m, float& v,
+                                           const StepScalars& s) {
+    const float mm = s.b1 * m + s.c1 * g;
+    const float vv = s.b2 * v + s.c2 * (g * g);
+    const float den = sqrtf(vv) / s.sbc2 + s.eps;
+    float pp = p - s.step_size * (mm / den);
+    if (s.has_decay) pp = pp - s.decay * pp;
+    m = mm;
+    v = vv;
+    p = pp;
+}
+
+__device__ __forceinline__ float abs_max4(float a, const float4& x) {
+    return fmaxf(fmaxf(a, fmaxf(fabsf(x.x), fabsf(x.y))), fmaxf(fabsf(x.z), fabsf(x.w)));
+}
+
+__device__ __forceinline__ uint32_t pack_codes(const float4& x, float scale) {
+    return e4m3_code(x.x / scale) | (e4m3_code(x.y / scale) << 8) |
+           (e4m3_code(x.z / scale) << 16) | (e4m3_code(x.w / scale) << 24);
+}
+
+// One workgroup owns one tile.  Pass 1 streams master/grad/m/v in with
+// coalesced 16-byte loads (thread t takes float4 t, t + 256, ...), updates
+// them in registers, writes master/m/v straight back and keeps the new
+// master values in registers.  The tile amax is reduced across the wave by
+// lane shuffles, then across the 4 waves through LDS (one barrier).  Pass 2
+// quantizes the register-held values: 4 codes per thread and float4, one
+// 32-bit store, so HBM sees each input once and each output once.
+__global__ __launch_bounds__(kThreads) void step_kernel(
+    float* __restrict__ master, const float* __restrict__ grad, float* __restrict__ mom1,
+    float* __restrict__ mom2, uint32_t* __restrict__ codes, float* __restrict__ scale_inv,
+    StepScalars s) {
+    __shared__ float wave_amax[kWaves];
+    const int64_t tile = blockIdx.x;
+    const int64_t base = tile * (kTileElems / 4);
+    float4* P = reinterpret_cast<float4*>(master) + base;
+    const float4* G = reinterpret_cast<const float4*>(grad) + base;
+    float4* M = reinterpret_cast<float4*>(mom1) + base;
+    float4* V = reinterpret_cast<float4*>(mom2) + base;
+
+    float4 keep[kStepVec];
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kStepVec; ++k) {
+        const int i = k * kThreads + threadIdx.x;
+        float4 p = P[i], m = M[i], v = V[i];
+        const float4 g = G[i];
+        adamw_elem(p.x, g.x, m.x, v.x, s);
+        adamw_elem(p.y, g.y, m.y, v.y, s);
+        adamw_elem(p.z, g.z, m.z, v.z, s);
+        adamw_elem(p.w, g.w, m.w, v.w, s);
+        M[i] = m;
+        V[i] = v;
+        P[i] = p;
+        keep[k] = p;
+        amax = abs_max4(amax, p);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    if ((threadIdx.x & 63) == 0) wave_amax[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = wave_amax[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) amax = fmaxf(amax, wave_amax[w]);
+
+    // scale_inv = amax / 448; an all-zero tile takes 1 and codes 0.
+    const bool zero = amax == 0.0f;
+    const float scale = zero ? 1.0f : amax / 448.0f;
+    if (threadIdx.x == 0) scale_inv[tile] = scale;
+    uint32_t* C = codes + base;
+#pragma unroll
+    for (int k = 0; k < kStepVec; ++k) {
+        const int i = k * kThreads + threadIdx.x;
+        C[i] = zero ? 0u : pack_codes(keep[k], scale);
+    }
+}
+
+// Fold: one workgroup per slot.  Thread t copies float4 column t % 32 of
+// rows t / 32, t / 32 + 8, ...: a wave covers two whole 512-byte tile rows
+// per load, so both the strided row-major reads and the contiguous tile
+// writes are coalesced.  Outside the weight's edge, and in padding slots,
+// the tile gets +0.0.
+__global__ __launch_bounds__(kThreads) void pack_kernel(const TileEntry* __restrict__ entries,
+                                                        float* __restrict__ dst, PackArgs args) {
+    const int64_t slot = blockIdx.x;
+    const TileEntry t = entries[slot];
+    float4* out = reinterpret_cast<float4*>(dst + slot * kTileElems);
+    const int c4 = threadIdx.x & 31;
+    const int r0 = threadIdx.x >> 5;
+    if (t.local < 0) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) out[(r0 + 8 * k) * 32 + c4] = make_float4(0.f, 0.f, 0.f, 0.f);
+        return;
+    }
+    const float* src = args.src[t.local] + t.base;
+    const bool vec = ((t.ld & 3) == 0) &&
+                     ((reinterpret_cast<uintptr_t>(args.src[t.local]) & 15u) == 0);
+    const int col = 4 * c4;
+    if (vec && t.valid_rows == kTileDim && t.valid_cols == kTileDim) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int r = r0 + 8 * k;
+            out[r * 32 + c4] = *reinterpret_cast<const float4*>(src + (int64_t)r * t.ld + col);
+        }
+        return;
+    }
+    for (int k = 0; k < 16; ++k) {
+        const int r = r0 + 8 * k;
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (r < t.valid_rows) {
+            const float* row = src + (int64_t)r * t.ld + col;
+            if (vec && col + 4 <= t.valid_cols) {
+                x = *reinterpret_cast<const float4*>(row);
+            } else {
+                if (col + 0 < t.valid_cols) x.x = row[0];
+                if (col + 1 < t.valid_cols) x.y = row[1];
+                if (col + 2 < t.valid_cols) x.z = row[2];
+                if (col + 3 < t.valid_cols) x.w = row[3];
+            }
+        }
+        out[r * 32 + c4] = x;
+    }
+}
+
+// Unfold of codes and scales: one workgroup per owned slot.  Thread t moves
+// 16 codes (column block t % 8) of rows t / 8, t / 8 + 32, ...; 16-byte
+// stores when the destination rows allow it, bytes at ragged edges.
+__global__ __launch_bounds__(kThreads) void unpack_kernel(const TileEntry* __restrict__ entries,
+                                                          const uint8_t* __restrict__ codes,
+                                                          const float* __restrict__ scale_inv,
+                                                          UnpackArgs args) {
+    const int64_t slot = blockIdx.x;
+    const TileEntry t = entries[slot];
+    if (t.local < 0) return;
+    const uint4* in = reinterpret_cast<const uint4*>(codes + slot * kTileElems);
+    uint8_t* dst = args.codes[t.local] + t.base;
+    const int c16 = threadIdx.x & 7;
+    const int r0 = threadIdx.x >> 3;
+    const int col = 16 * c16;
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(args.codes[t.local]);
+    const bool vec16 = ((t.ld & 15) == 0) && ((addr & 15u) == 0);
+    const bool vec4 = ((t.ld & 3) == 0) && ((addr & 3u) == 0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int r = r0 + 32 * k;
+        if (r >= t.valid_rows) break;
+        const uint4 x = in[r * 8 + c16];
+        uint8_t* row = dst + (int64_t)r * t.ld + col;
+        if (col + 16 <= t.valid_cols && vec16) {
+            *reinterpret_cast<uint4*>(row) = x;
+        } else if (col + 16 <= t.valid_cols && vec4) {
+            uint32_t* r4 = reinterpret_cast<uint32_t*>(row);
+            r4[0] = x.x;
+            r4[1] = x.y;
+            r4[2] = x.z;
+            r4[3] = x.w;
+        } else {
+            for (int b = 0; b < 16 && col + b < t.valid_cols; ++b) {
+                const uint32_t w = b < 4 ? x.x : b < 8 ? x.y : b < 12 ? x.z : x.w;
+                row[b] = (uint8_t)(w >> (8 * (b & 3)));
+            }
+        }
+    }
+    if (threadIdx.x == 0) args.scale[t.local][t.scale_index] = scale_inv[slot];
+}
+
+__global__ __launch_bounds__(kThreads) void encode_kernel(const float* __restrict__ in,
+                                                          uint8_t* __restrict__ out, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride)
+        out[i] = (uint8_t)e4m3_code(in[i]);
+}
+
+}  // namespace
+
+int launch_step(float* master, const float* grad, float* m, float* v, uint8_t* codes,
+                float* scale_inv, int64_t n_tiles, const StepScalars& s, void* stream) {
+    if (n_tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(step_kernel, dim3((uint32_t)n_tiles), dim3(kThreads), 0,
+                       (hipStream_t)stream, master, grad, m, v,
+                       reinterpret_cast<uint32_t*>(codes), scale_inv, s);
+    return hipGetLastError();
+}
+
+int launch_pack(const TileEntry* d_entries, int64_t n_slots, float* dst, const PackArgs& args,
+                void* stream) {
+    if (n_slots == 0) return hipSuccess;
+    hipLaunchKernelGGL(pack_kernel, dim3((uint32_t)n_slots), dim3(kThreads), 0,
+                       (hipStream_t)stream, d_entries, dst, args);
+    return hipGetLastError();
+}
+
+int launch_unpack(const TileEntry* d_entries, int64_t n_slots, const uint8_t* codes,
+                  const float* scale_inv, const UnpackArgs& args, void* stream) {
+    if (n_slots == 0) return hipSuccess;
+    hipLaunchKernelGGL(unpack_kernel, dim3((uint32_t)n_slots), dim3(kThreads), 0,
+                       (hipStream_t)stream, d_entries, codes, scale_inv, args);
+    return hipGetLastError();
+}
+
+int launch_encode(const float* in, uint8_t* out, int64_t n, void* stream) {
+    if (n == 0) return hipSuccess;
+    int64_t blocks = (n + kThreads - 1) / kThreads;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(encode_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0,
+                       (hipStream_t)stream, in, out, n);
+    return hipGetLastError();
+}
+
+const char* hip_error_string(int err) { return hipGetErrorString((hipError_t)err); }
+
+}  // namespace bfz

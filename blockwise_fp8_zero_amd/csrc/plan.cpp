@@ -1,0 +1,172 @@
+// Host planner: the block-wise split of one rank and its lookup table.
+//
+// "A ZeRO Optimizer Design for Blockwise FP8 Quantization", section
+// "Block-wise split": weights are cut at 128x128 units (each quantized
+// dimension padded to a multiple of 128), and a lookup table records, for
+// every unit in the flat buffer, its weight and its real extent, so the
+// optimizer can walk the 1-D buffer.  Section "Parameter layout transform"
+// fixes the unit order within a weight (expert, tile row, tile column).
+// Dealing units to ranks: equal quota q = ceil(T / D), rank r takes the
+// contiguous global range [r q, min((r + 1) q, T)), short shards padded to q
+// (the page pads param-wise buckets to the largest one, section
+// "Param-wise split"; contiguity keeps the rank's slice one range of the
+// flat buffer, so one collective moves it).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <limits>
+#include <new>
+
+#include "bfz_internal.h"
+
+namespace {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" int bfz_plan_create(const int64_t* dims, int32_t n_weights, int32_t D, int32_t rank,
+                               bfz_plan** out) {
+    using namespace bfz;
+    if (!dims || !out) return fail(BFZ_EINVAL, "bfz_plan_create: null pointer");
+    *out = nullptr;
+    if (n_weights < 1) return fail(BFZ_EINVAL, "bfz_plan_create: n_params must be >= 1");
+    if (D < 1 || rank < 0 || rank >= D)
+        return fail(BFZ_EINVAL, "bfz_plan_create: need D >= 1 and 0 <= rank < D (got D=%d rank=%d)",
+                    D, rank);
+    const int64_t kMaxDim = std::numeric_limits<int32_t>::max();
+    int64_t total = 0;
+    for (int32_t p = 0; p < n_weights; ++p) {
+        int64_t E = dims[3 * p], H = dims[3 * p + 1], W = dims[3 * p + 2];
+        if (E < 1 || H < 1 || W < 1 || H > kMaxDim || W > kMaxDim)
+            return fail(BFZ_EINVAL, "bfz_plan_create: weight %d has bad dims {%lld, %lld, %lld}", p,
+                        (long long)E, (long long)H, (long long)W);
+        int64_t grid = ceil_div(H, kTileDim) * ceil_div(W, kTileDim);
+        if (E > (int64_t(1) << 40) / grid)
+            return fail(BFZ_EINVAL, "bfz_plan_create: weight %d has too many tiles", p);
+        total += E * grid;
+    }
+
+    bfz_plan* plan = new (std::nothrow) bfz_plan;
+    if (!plan) return fail(BFZ_EINVAL, "bfz_plan_create: out of host memory");
+    plan->n_weights = n_weights;
+    plan->D = D;
+    plan->rank = rank;
+    plan->dims.assign(dims, dims + 3 * n_weights);
+    plan->total = total;
+    plan->quota = ceil_div(total, D);
+    plan->first = int64_t(rank) * plan->quota;
+    int64_t last = std::min(plan->first + plan->quota, total);
+    plan->owned = last > plan->first ? last - plan->first : 0;
+
+    const int64_t q = plan->quota;
+    plan->table.assign(6 * q, 0);
+    plan->entries.assign(q, TileEntry{0, 0, 0, 0, 0, -1, 0});
+    for (int64_t s = 0; s < q; ++s) plan->table[6 * s] = -1;
+
+    // Walk the owned global range weight by weight; within a weight, the
+    // global index g maps to (expert, tile row, tile col) by division.
+    int64_t weight_first = 0;  // global index of weight p's first tile
+    std::vector<int32_t> slot_weight(q, -1);
+    for (int32_t p = 0; p < n_weights && weight_first < last; ++p) {
+        int64_t E = dims[3 * p], H = dims[3 * p + 1], W = dims[3 * p + 2];
+        int64_t hb = ceil_div(H, kTileDim), wb = ceil_div(W, kTileDim);
+        int64_t n = E * hb * wb;
+        int64_t lo = std::max(weight_first, plan->first), hi = std::min(weight_first + n, last);
+        for (int64_t g = lo; g < hi; ++g) {
+            int64_t local = g - weight_first;
+            int64_t e = local / (hb * wb), rem = local % (hb * wb);
+            int64_t i = rem / wb, j = rem % wb;
+            int64_t s = g - plan->first;
+            int64_t rows = std::min<int64_t>(kTileDim, H - kTileDim * i);
+            int64_t cols = std::min<int64_t>(kTileDim, W - kTileDim * j);
+            int64_t* row = &plan->table[6 * s];
+            row[0] = p; row[1] = e; row[2] = i; row[3] = j; row[4] = rows; row[5] = cols;
+            TileEntry& t = plan->entries[s];
+            t.base = (e * H + kTileDim * i) * W + kTileDim * j;
+            t.ld = int32_t(W);
+            t.scale_index = int32_t((e * hb + i) * wb + j);
+            t.valid_rows = int16_t(rows);
+            t.valid_cols = int16_t(cols);
+            slot_weight[s] = p;
+        }
+        weight_first += n;
+    }
+
+    // Cut the slots into launch segments of at most kSegWeights weights.
+    int64_t s = 0;
+    while (s < plan->owned) {
+        Segment seg{s, 0, slot_weight[s], 0};
+        int64_t e = s;
+        while (e < plan->owned && slot_weight[e] - seg.weight0 < kSegWeights) ++e;
+        seg.n_slots = e - s;
+        seg.n_weights = slot_weight[e - 1] - seg.weight0 + 1;
+        for (int64_t k = s; k < e; ++k)
+            plan->entries[k].local = int16_t(slot_weight[k] - seg.weight0);
+        plan->segments.push_back(seg);
+        s = e;
+    }
+    if (plan->owned < q) {  // padding slots ride in a segment of their own
+        plan->segments.push_back(Segment{plan->owned, q - plan->owned, 0, 0});
+    }
+    *out = plan;
+    return BFZ_OK;
+}
+
+extern "C" void bfz_plan_destroy(bfz_plan* plan) {
+    if (!plan) return;
+    if (plan->d_entries) {
+        int prev = -1;
+        (void)hipGetDevice(&prev);
+        if (plan->device >= 0) (void)hipSetDevice(plan->device);
+        (void)hipFree(plan->d_entries);
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+    delete plan;
+}
+
+extern "C" int bfz_plan_upload(bfz_plan* plan) {
+    using namespace bfz;
+    if (!plan) return fail(BFZ_EINVAL, "bfz_plan_upload: null plan");
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return fail(BFZ_EHIP, "bfz_plan_upload: %s", hipGetErrorString(err));
+    if (plan->d_entries) {
+        if (plan->device == dev) return BFZ_OK;
+        return fail(BFZ_EINVAL, "bfz_plan_upload: plan already on device %d", plan->device);
+    }
+    size_t bytes = std::max<size_t>(1, plan->entries.size()) * sizeof(TileEntry);
+    TileEntry* d = nullptr;
+    err = hipMalloc(reinterpret_cast<void**>(&d), bytes);
+    if (err != hipSuccess) return fail(BFZ_EHIP, "bfz_plan_upload: hipMalloc: %s", hipGetErrorString(err));
+    if (!plan->entries.empty()) {
+        err = hipMemcpy(d, plan->entries.data(), plan->entries.size() * sizeof(TileEntry),
+                        hipMemcpyHostToDevice);
+        if (err != hipSuccess) {
+            (void)hipFree(d);
+            return fail(BFZ_EHIP, "bfz_plan_upload: hipMemcpy: %s", hipGetErrorString(err));
+        }
+    }
+    plan->d_entries = d;
+    plan->device = dev;
+    return BFZ_OK;
+}
+
+extern "C" int64_t bfz_plan_shard_tiles(const bfz_plan* plan) { return plan ? plan->quota : -1; }
+extern "C" int64_t bfz_plan_owned_tiles(const bfz_plan* plan) { return plan ? plan->owned : -1; }
+extern "C" int64_t bfz_plan_total_tiles(const bfz_plan* plan) { return plan ? plan->total : -1; }
+
+extern "C" int bfz_plan_table(const bfz_plan* plan, int64_t* out) {
+    if (!plan || !out) return bfz::fail(BFZ_EINVAL, "bfz_plan_table: null pointer");
+    std::copy(plan->table.begin(), plan->table.end(), out);
+    return BFZ_OK;
+}
+
+extern "C" int bfz_plan_tile(const bfz_plan* plan, int64_t slot, int64_t out[6]) {
+    if (!plan || !out) return bfz::fail(BFZ_EINVAL, "bfz_plan_tile: null pointer");
+    if (slot < 0 || slot >= plan->quota)
+        return bfz::fail(BFZ_EINVAL, "bfz_plan_tile: slot %lld outside [0, %lld)", (long long)slot,
+                         (long long)plan->quota);
+    std::copy(&plan->table[6 * slot], &plan->table[6 * slot] + 6, out);
+    return BFZ_OK;
+}

@@ -1,0 +1,172 @@
+/*
+ * bfz.h -- C ABI of the block-wise FP8 ZeRO-1 shard step on MI355X (gfx950).
+ *
+ * One data-parallel rank owns a contiguous run of whole 128x128 weight tiles
+ * (the block-wise split of "A ZeRO Optimizer Design for Blockwise FP8
+ * Quantization", section "Block-wise split").  Per optimizer step it
+ *   1. folds its row-major FP32 gradients into tile-major order (pack_shard;
+ *      the fold of section "Parameter layout transform"),
+ *   2. runs AdamW on the FP32 master weights and moments of those tiles and
+ *      re-quantizes every updated tile to E4M3 with one scale per tile,
+ *      scale_inv = amax / 448 (adamw_fp8_step; the update and quantization
+ *      steps of section "Summary", the AdamW of section 4.3 of the lpnh.cn
+ *      optimizer-state quantization essay, the per-tile scale and quantizer
+ *      of "FP8-Flow-MoE", section 3.1),
+ *   3. unfolds the codes and scales back to row-major FP8 weights and the
+ *      row-major scale grid (unpack_fp8; the unfold of "Parameter layout
+ *      transform" and "Summary").
+ *
+ * Conventions shared by every call:
+ *   - A tile is 16384 contiguous elements: 128 rows of 128, row-major.
+ *     A shard is q tiles back to back (q = bfz_plan_shard_tiles).
+ *   - Device pointers are caller-owned (the library never frees them); the
+ *     library allocates only the plan's small device table, in
+ *     bfz_plan_upload, freed by bfz_plan_destroy.
+ *   - pack_shard, adamw_fp8_step and unpack_fp8 are asynchronous on the HIP
+ *     stream passed as `stream` (NULL = the null stream): they only enqueue
+ *     kernels, never allocate, never synchronize.
+ *   - Return value: 0 on success, else a negative BFZ_E* code; the message
+ *     for the calling thread's last failure is bfz_last_error().
+ *   - Non-finite inputs (NaN, Inf) give unspecified results.
+ */
+#ifndef BFZ_H
+#define BFZ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BFZ_TILE_DIM 128
+#define BFZ_TILE_ELEMS 16384
+
+#define BFZ_OK 0
+#define BFZ_EINVAL (-1) /* null pointer, bad size or shape, bad hyper-parameter */
+#define BFZ_EALIGN (-2) /* a pointer lacks its required alignment */
+#define BFZ_EHIP (-3)   /* a HIP runtime call or kernel launch failed */
+#define BFZ_ESTATE (-4) /* plan used before bfz_plan_upload */
+
+/* The block-wise split of one rank: the lookup table of its tiles. */
+typedef struct bfz_plan bfz_plan;
+
+/* AdamW hyper-parameters.  step is the counter t >= 1 of the step being
+ * taken (the first step is t = 1).  Requires lr, eps, weight_decay finite,
+ * eps >= 0, 0 <= beta1 < 1, 0 <= beta2 < 1. */
+typedef struct {
+    double lr, beta1, beta2, eps, weight_decay;
+    int64_t step;
+} bfz_adamw;
+
+/*
+ * Build rank `rank`'s block-wise split of n_params weights.
+ * dims: host array of n_params triples {E, H, W}: weight p is a row-major
+ * FP32 tensor of E experts of H x W (E = 1 for a plain matrix), all >= 1.
+ * Every weight is cut into ceil(H/128) x ceil(W/128) tiles per expert, the
+ * last row / column of tiles zero-padded.  Tiles are numbered through all
+ * weights in the order given, and within a weight by (expert, tile row,
+ * tile column) -- the fold order.  With T tiles in all, every rank gets the
+ * same quota q = ceil(T / D) and rank r owns global tiles
+ * [r q, min((r + 1) q, T)); a shorter shard ends in all-zero padding slots
+ * so that every shard is q tiles (section "Block-wise split" pads buckets to
+ * the largest one; the contiguous equal quota is this library's reading of
+ * how the page deals tiles to ranks).  Host only: touches no GPU.
+ * On success *out receives a new plan.  Errors: BFZ_EINVAL for null
+ * pointers, n_params < 1, D < 1, rank outside [0, D), a dimension < 1, or
+ * H, W > 2^31 - 1.
+ */
+int bfz_plan_create(const int64_t* dims, int32_t n_params, int32_t D, int32_t rank,
+                    bfz_plan** out);
+
+/* Copy the plan's tile table to the current HIP device (allocates about
+ * 24 bytes per tile; synchronous).  Needed once before pack_shard or
+ * unpack_fp8.  Errors: BFZ_EINVAL (null), BFZ_EHIP. */
+int bfz_plan_upload(bfz_plan* plan);
+
+/* Free the plan and its device table.  NULL is accepted. */
+void bfz_plan_destroy(bfz_plan* plan);
+
+/* q: slots in the shard (owned tiles plus padding slots). */
+int64_t bfz_plan_shard_tiles(const bfz_plan* plan);
+/* Tiles the rank actually owns (<= q); slots [owned, q) are padding. */
+int64_t bfz_plan_owned_tiles(const bfz_plan* plan);
+/* T: tiles of all weights, over all ranks. */
+int64_t bfz_plan_total_tiles(const bfz_plan* plan);
+
+/* Host copy of the lookup table: out receives q rows of
+ * {param, expert, tile_row, tile_col, valid_rows, valid_cols}; a padding
+ * slot reads {-1, 0, 0, 0, 0, 0}.  bfz_plan_tile reads one slot.
+ * Errors: BFZ_EINVAL (null, slot outside [0, q)). */
+int bfz_plan_table(const bfz_plan* plan, int64_t* out);
+int bfz_plan_tile(const bfz_plan* plan, int64_t slot, int64_t out[6]);
+
+/*
+ * Fold: dst[s][a][b] = src[p][e][128 i + a][128 j + b] for the weight p,
+ * expert e and tile (i, j) of slot s, and +0.0 outside the weight's edge
+ * and in padding slots.
+ * src: host array of n_params device pointers (the plan's weight order); an
+ *      entry may be NULL when the rank owns none of that weight's tiles.
+ *      Each weight is read, never written; 4-byte alignment is enough (a
+ *      16-byte aligned weight whose W is a multiple of 4 takes the
+ *      vector path).
+ * dst: device buffer of q * 16384 floats, 16-byte aligned, written whole.
+ * Errors: BFZ_EINVAL (null plan / dst, NULL src entry of an owned weight),
+ *         BFZ_EALIGN, BFZ_ESTATE, BFZ_EHIP.
+ */
+int pack_shard(const bfz_plan* plan, const float* const* src, float* dst, void* stream);
+
+/*
+ * One fused optimizer step over n_tiles whole tiles (n_tiles * 16384
+ * elements per array), all device buffers:
+ *   per element, FP32:  m = b1 m + (1 - b1) g
+ *                       v = b2 v + (1 - b2) g^2
+ *                       p = p - (lr / (1 - b1^t)) m / (sqrt(v) / sqrt(1 - b2^t) + eps)
+ *                       p = p - lr wd p          (when wd != 0; on the updated p)
+ *   per tile:           amax = max |p|;  scale_inv = amax / 448, or 1 when amax == 0
+ *   per element:        code = E4M3(p / scale_inv), 0 in an all-zero tile,
+ * where E4M3 is round-to-nearest (ties to even) onto the OCP E4M3FN values,
+ * saturating at +-448, keeping the sign (tiny negatives give 0x80).
+ * The per-step scalars (1 - b1, lr / (1 - b1^t), sqrt(1 - b2^t), lr wd, ...)
+ * are formed in double on the host and rounded once to FP32; every element
+ * operation is a single IEEE binary32 operation (no fused multiply-add,
+ * correctly rounded sqrt and divide).
+ * master, m, v: read and overwritten in place (16-byte aligned).
+ * grad: read only (16-byte aligned).  codes: n_tiles * 16384 bytes written
+ * (16-byte aligned).  scale_inv: n_tiles floats written (4-byte aligned).
+ * n_tiles = 0 is a no-op.  Padding tiles (all zero) stay zero and give
+ * scale_inv 1 and codes 0.
+ * Errors: BFZ_EINVAL (null pointer, n_tiles < 0, bad hyper-parameters),
+ *         BFZ_EALIGN, BFZ_EHIP.
+ */
+int adamw_fp8_step(float* master, const float* grad, float* m, float* v, uint8_t* codes,
+                   float* scale_inv, int64_t n_tiles, const bfz_adamw* hp, void* stream);
+
+/*
+ * Unfold of the rank's owned slots: dst_fp8[p][e][128 i + a][128 j + b] =
+ * codes[s][a][b] inside the weight's edge, and dst_scale[p][(e hb + i) wb + j]
+ * = scale_inv[s] (hb = ceil(H/128), wb = ceil(W/128): the row-major scale
+ * grid [E, hb, wb]).  Elements of tiles other ranks own are not touched.
+ * codes: q * 16384 bytes (16-byte aligned); scale_inv: q floats.
+ * dst_fp8 / dst_scale: host arrays of n_params device pointers; entries of
+ * weights the rank does not touch may be NULL.  Any alignment is accepted
+ * (16-byte aligned rows take the vector path).
+ * Errors: BFZ_EINVAL, BFZ_EALIGN, BFZ_ESTATE, BFZ_EHIP.
+ */
+int unpack_fp8(const bfz_plan* plan, const uint8_t* codes, const float* scale_inv,
+               uint8_t* const* dst_fp8, float* const* dst_scale, void* stream);
+
+/*
+ * The E4M3 rounding adamw_fp8_step applies to p / scale_inv, exposed on
+ * its own so it can be checked over every fp32 bit pattern:
+ * out[k] = E4M3(in[k]) for k < n.  Device buffers, any alignment.
+ * Errors: BFZ_EINVAL (null, n < 0), BFZ_EHIP.
+ */
+int bfz_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* bfz_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BFZ_H */

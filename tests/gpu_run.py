@@ -1,0 +1,107 @@
+"""Drive one workload through the HIP path (product calls only, no oracle).
+
+Inputs are row-major FP32 weights drawn on the device by the seeded
+generator; the path then folds them (pack_shard), steps (adamw_fp8_step)
+and unfolds (unpack_fp8), exactly as a rank would.
+"""
+import numpy as np
+import torch
+
+import blockwise_fp8_zero_amd as bfz
+import synth
+from synth import workloads as WL
+
+TILE_ELEMS = bfz.TILE_ELEMS
+
+
+def hp_for(w, t):
+    return bfz.AdamW(step=t, **WL.HP)
+
+
+class GpuWorkload:
+    """Device state of one rank's shard of workload w."""
+
+    def __init__(self, w: WL.Workload, device="cuda"):
+        self.w = w
+        self.device = torch.device(device)
+        with torch.cuda.device(self.device):
+            self.plan = bfz.Plan(w.dims, w.D, w.rank)
+        self.q = self.plan.shard_tiles
+        self.owned = self.plan.owned_tiles
+        self.table = self.plan.table()
+        owned_rows = self.table[:self.owned]
+        self.touched = sorted({int(p) for p in owned_rows[:, 0]})
+        self.ranges = {p: WL.rows_touched(owned_rows, p, w.dims) for p in self.touched}
+        n = self.q * TILE_ELEMS
+        kw = dict(device=self.device)
+        self.master = torch.empty(n, dtype=torch.float32, **kw)
+        self.grad = torch.empty(n, dtype=torch.float32, **kw)
+        self.m = torch.empty(n, dtype=torch.float32, **kw)
+        self.v = torch.empty(n, dtype=torch.float32, **kw)
+        self.codes = torch.empty(n, dtype=torch.uint8, **kw)
+        self.scale_inv = torch.empty(self.q, dtype=torch.float32, **kw)
+        self.grad_rm = None
+        self.t_done = 0
+
+    # ---- inputs ------------------------------------------------------------
+    def _rowmajor(self, tensor, step=0):
+        """Row-major device buffers of every touched weight, drawn over the
+        rows the rank's tiles cover (other rows are never read)."""
+        bufs = [None] * len(self.w.dims)
+        for p in self.touched:
+            lo, hi = self.ranges[p]
+            b = torch.empty(self.w.numel(p), dtype=torch.float32, device=self.device)
+            synth.fill_device(self.w.recipe(tensor, p, step), b[lo:hi], lo, hi)
+            bufs[p] = b
+        return bufs
+
+    def load_state(self):
+        """Fold the initial master, m and v into the shard."""
+        for tensor, dst in ((WL.MASTER, self.master), (WL.MOM1, self.m), (WL.MOM2, self.v)):
+            srcs = self._rowmajor(tensor)
+            bfz.pack_shard(self.plan, srcs, dst)
+            del srcs
+        torch.cuda.synchronize(self.device)
+
+    def draw_grads(self, t):
+        self.grad_rm = self._rowmajor(WL.GRAD, t)
+
+    # ---- the path ------------------------------------------------------------
+    def pack_grads(self):
+        bfz.pack_shard(self.plan, self.grad_rm, self.grad)
+
+    def step(self, t):
+        bfz.adamw_fp8_step(self.master, self.grad, self.m, self.v, self.codes, self.scale_inv,
+                           hp_for(self.w, t))
+
+    def run_steps(self, steps=None):
+        """Draw, fold and apply the grads of each step counter in `steps`."""
+        for t in (steps if steps is not None else self.w.steps):
+            self.draw_grads(t)
+            self.pack_grads()
+            self.step(t)
+            self.t_done = t
+        torch.cuda.synchronize(self.device)
+
+    def alloc_rowmajor_out(self):
+        fp8 = [None] * len(self.w.dims)
+        sc = [None] * len(self.w.dims)
+        for p in self.touched:
+            E, H, W = self.w.dims[p]
+            fp8[p] = torch.zeros(E * H * W, dtype=torch.uint8, device=self.device)
+            sc[p] = torch.zeros(E * (-(-H // 128)) * (-(-W // 128)), dtype=torch.float32,
+                                device=self.device)
+        return fp8, sc
+
+    def unpack(self, fp8, sc):
+        bfz.unpack_fp8(self.plan, self.codes, self.scale_inv, fp8, sc)
+
+    # ---- read back ---------------------------------------------------------
+    def tiles(self, slots):
+        idx = torch.as_tensor(np.asarray(slots, dtype=np.int64), device=self.device)
+
+        def take(x):
+            return x.view(-1, TILE_ELEMS).index_select(0, idx).cpu().numpy()
+
+        return dict(master=take(self.master), m=take(self.m), v=take(self.v),
+                    codes=take(self.codes), scale_inv=self.scale_inv[idx].cpu().numpy())

@@ -1,0 +1,109 @@
+"""The C ABI on the CPU: the library loads, exports every function
+include/bfz.h declares, plans exactly like the oracle, and rejects bad
+arguments before touching any GPU.  No compute call runs here."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import blockwise_fp8_zero_amd as bfz
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "bfz.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(\w+)\s*\(", text, flags=re.M)
+    return sorted({n for n in names if n not in ("if", "defined")})
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert {"pack_shard", "adamw_fp8_step", "unpack_fp8", "bfz_plan_create",
+            "bfz_last_error"} <= set(names)
+    L = bfz.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_plan_matches_oracle_plan():
+    rng = np.random.default_rng(0)
+    for trial in range(40):
+        dims = [(int(rng.integers(1, 4)), int(rng.integers(1, 900)), int(rng.integers(1, 900)))
+                for _ in range(int(rng.integers(1, 7)))]
+        D = int(rng.integers(1, 10))
+        for r in range(D):
+            q, owned, table = oracle.plan(dims, D, r)
+            p = bfz.Plan(dims, D, r, upload=False)
+            assert (p.shard_tiles, p.owned_tiles, p.total_tiles) == (q, owned, oracle.total_tiles(dims))
+            assert np.array_equal(p.table(), table)
+            if q:
+                assert p.tile(q - 1) == tuple(table[q - 1])
+            p.close()
+
+
+def test_plan_of_the_workloads():
+    from synth import workloads as WL
+    for f in WL.ALL:
+        w = f()
+        q, owned, table = oracle.plan(w.dims, w.D, w.rank)
+        p = bfz.Plan(w.dims, w.D, w.rank, upload=False)
+        assert p.shard_tiles == q and p.owned_tiles == owned
+        assert np.array_equal(p.table(), table), w.name
+
+
+@pytest.mark.parametrize("dims,D,rank", [
+    ([(1, 10, 10)], 0, 0), ([(1, 10, 10)], 2, 2), ([(1, 10, 10)], 2, -1),
+    ([(0, 10, 10)], 1, 0), ([(1, 10, -3)], 1, 0), ([(1, 2 ** 31, 5)], 1, 0), ([], 1, 0),
+])
+def test_plan_rejects_bad_arguments(dims, D, rank):
+    with pytest.raises(bfz.BfzError) as e:
+        bfz.Plan(dims, D, rank, upload=False)
+    assert e.value.code == bfz.BFZ_EINVAL
+    assert bfz.lib().bfz_last_error()
+
+
+def _call_step(ptrs, n_tiles=1, hp=None):
+    hp = hp or bfz.AdamW(lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1)
+    return bfz.lib().adamw_fp8_step(*[C.c_void_p(p) for p in ptrs], n_tiles, C.byref(hp), None)
+
+
+def test_step_argument_errors_without_gpu():
+    ok = [0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000]
+    assert _call_step([0] + ok[1:]) == bfz.BFZ_EINVAL
+    assert _call_step(ok, n_tiles=-1) == bfz.BFZ_EINVAL
+    assert _call_step(ok, n_tiles=1 << 31) == bfz.BFZ_EINVAL
+    for k in range(5):
+        bad = list(ok)
+        bad[k] += 4
+        assert _call_step(bad) == bfz.BFZ_EALIGN
+        assert "aligned" in bfz.lib().bfz_last_error().decode()
+    bad = list(ok)
+    bad[5] += 2
+    assert _call_step(bad) == bfz.BFZ_EALIGN
+    for field, val in (("beta1", 1.0), ("beta2", -0.1), ("eps", -1.0), ("lr", float("nan")),
+                       ("step", 0), ("weight_decay", float("inf"))):
+        hp = bfz.AdamW(lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1)
+        setattr(hp, field, val)
+        assert _call_step(ok, hp=hp) == bfz.BFZ_EINVAL, field
+
+
+def test_pack_unpack_errors_without_gpu():
+    L = bfz.lib()
+    p = bfz.Plan([(1, 256, 256), (1, 128, 128)], 2, 0, upload=False)
+    src = (C.c_void_p * 2)(0x10000, 0x20000)
+    # not uploaded
+    assert L.pack_shard(p.handle, C.cast(src, C.c_void_p), C.c_void_p(0x30000), None) == bfz.BFZ_ESTATE
+    assert L.pack_shard(p.handle, None, C.c_void_p(0x30000), None) == bfz.BFZ_EINVAL
+    assert L.pack_shard(None, C.cast(src, C.c_void_p), C.c_void_p(0x30000), None) == bfz.BFZ_EINVAL
+    d8 = (C.c_void_p * 2)(0x10000, 0x20000)
+    assert L.unpack_fp8(p.handle, C.c_void_p(0x40000), C.c_void_p(0x50000), C.cast(d8, C.c_void_p),
+                        C.cast(d8, C.c_void_p), None) == bfz.BFZ_ESTATE
+    assert L.bfz_e4m3_encode(None, C.c_void_p(0x10), 5, None) == bfz.BFZ_EINVAL
+    assert L.bfz_e4m3_encode(C.c_void_p(0x10), C.c_void_p(0x10), -1, None) == bfz.BFZ_EINVAL
+    assert L.bfz_plan_tile(p.handle, 99, C.cast((C.c_int64 * 6)(), C.c_void_p)) == bfz.BFZ_EINVAL
+    p.close()

@@ -1,0 +1,218 @@
+"""GPU parity of the HIP path against the oracle (needs an MI355X).
+
+Every case prints its name, workload and seed before touching the GPU.
+Sizes: the tiny and ragged workloads are compared element by element on
+every slot; the dense-LLM, MoE and large workloads run at full size in
+the launch configuration the benchmark times, and a sample of slots
+(first, last, padding, ragged edges, weight boundaries, zero tiles and a
+seeded random set) is recomputed by the oracle from regenerated inputs.
+"""
+import gc
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import blockwise_fp8_zero_amd as bfz
+import oracle
+from synth import workloads as WL
+from tests.compare import compare
+from tests.gpu_run import GpuWorkload
+from tests.oracle_run import oracle_slots, sample_slots
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[gpu-parity]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _free():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _check(gpu, ora, what):
+    rep = compare(gpu, ora)
+    _say(what, {k: v for k, v in rep.items() if k != "fail"})
+    assert rep["ok"], (what, rep["fail"])
+    return rep
+
+
+def test_tiny_every_step_every_slot():
+    w = WL.tiny()
+    _say("tiny: 256x384, 3 steps, seed", w.seed)
+    g = GpuWorkload(w)
+    g.load_state()
+    slots = list(range(g.q))
+    for k, t in enumerate(w.steps):
+        g.run_steps([t])
+        ora = oracle_slots(w, slots, steps=w.steps[:k + 1])
+        rep = _check(g.tiles(slots), ora, f"tiny after t={t}")
+        assert rep["exact"], "the step is expected to be bit-exact with the oracle"
+    # unfold of the final codes and scales
+    fp8, sc = g.alloc_rowmajor_out()
+    g.unpack(fp8, sc)
+    q, owned, table = oracle.plan(w.dims, w.D, w.rank)
+    E, H, W = w.dims[0]
+    o8 = np.zeros((E, H, W), dtype=np.uint8)
+    osc = np.zeros((E, 2, 3), dtype=np.float32)
+    oracle.unpack(w.dims, ora["codes"].reshape(-1), ora["scale_inv"], table, [o8], [osc])
+    assert np.array_equal(fp8[0].cpu().numpy().reshape(E, H, W), o8)
+    assert np.array_equal(sc[0].cpu().numpy().reshape(E, 2, 3), osc)
+
+
+def test_ragged_every_slot():
+    w = WL.ragged()
+    _say("ragged: 40 matrices, D=8 rank 3, seed", w.seed)
+    g = GpuWorkload(w)
+    g.load_state()
+    g.run_steps()
+    slots = list(range(g.q))
+    ora = oracle_slots(w, slots)
+    rep = _check(g.tiles(slots), ora, "ragged")
+    assert rep["exact"]
+    # unfold into the ragged row-major weights
+    fp8, sc = g.alloc_rowmajor_out()
+    g.unpack(fp8, sc)
+    q, owned, table = oracle.plan(w.dims, w.D, w.rank)
+    o8 = [None] * len(w.dims)
+    osc = [None] * len(w.dims)
+    for p in g.touched:
+        E, H, W = w.dims[p]
+        o8[p] = np.zeros((E, H, W), dtype=np.uint8)
+        osc[p] = np.zeros((E, -(-H // 128), -(-W // 128)), dtype=np.float32)
+    oracle.unpack(w.dims, ora["codes"].reshape(-1), ora["scale_inv"], table, o8, osc)
+    for p in g.touched:
+        assert np.array_equal(fp8[p].cpu().numpy().reshape(o8[p].shape), o8[p]), p
+        assert np.array_equal(sc[p].cpu().numpy().reshape(osc[p].shape), osc[p]), p
+    del g
+    _free()
+
+
+@pytest.mark.parametrize("name", ["dense_llm", "moe_experts", "large"])
+def test_full_size_sampled(name):
+    w = WL.BY_NAME[name]()
+    _say(name, "full size,", len(w.dims), "weights, D =", w.D, "rank", w.rank, "seed", w.seed)
+    g = GpuWorkload(w)
+    g.load_state()
+    g.run_steps()
+    slots = sample_slots(w)
+    _say(name, "slots sampled:", len(slots), "of", g.q)
+    ora = oracle_slots(w, slots)
+    rep = _check(g.tiles(slots), ora, name)
+    assert rep["exact"]
+    if name == "large":
+        # amax = 0 guard on the all-zero tiles of this workload
+        zero = [k for k, s in enumerate(slots) if not ora["master"][k].any()]
+        assert zero, "sample holds no all-zero tile"
+        assert (ora["scale_inv"][zero] == 1.0).all()
+        # row-major FP8 + scale grid, checked at the sampled tiles
+        fp8, sc = g.alloc_rowmajor_out()
+        g.unpack(fp8, sc)
+        torch.cuda.synchronize()
+        for k, s in enumerate(slots):
+            p, e, i, j, vr, vc = (int(x) for x in ora["table"][k])
+            if p < 0:
+                continue
+            E, H, W = w.dims[p]
+            block = fp8[p].view(E, H, W)[e, 128 * i:128 * i + vr, 128 * j:128 * j + vc]
+            want = ora["codes"][k].reshape(128, 128)[:vr, :vc]
+            assert np.array_equal(block.cpu().numpy(), want), (s, p, e, i, j)
+            hb, wb = -(-H // 128), -(-W // 128)
+            assert float(sc[p][(e * hb + i) * wb + j]) == float(ora["scale_inv"][k])
+    del g
+    _free()
+
+
+def test_rank_decomposition_is_invariant():
+    """Every tile's result is independent of which rank owns it: the union
+    of the D shards equals the single-rank run, bit for bit."""
+    w1 = WL.ragged()
+    w1.dims = w1.dims[:6]
+    w1.D, w1.rank = 1, 0
+    _say("rank invariance: 6 ragged matrices, D in {1, 3, 7}")
+    ref = GpuWorkload(w1)
+    ref.load_state()
+    ref.run_steps()
+    full = ref.tiles(list(range(ref.owned)))
+    for D in (3, 7):
+        parts = []
+        for r in range(D):
+            w = WL.ragged()
+            w.dims, w.D, w.rank = w1.dims, D, r
+            g = GpuWorkload(w)
+            g.load_state()
+            g.run_steps()
+            if g.owned:
+                parts.append(g.tiles(list(range(g.owned))))
+            pad = list(range(g.owned, g.q))
+            if pad:  # padding slots: zeros, scale 1, codes 0
+                t = g.tiles(pad)
+                assert not t["master"].any() and not t["codes"].any()
+                assert (t["scale_inv"] == 1.0).all()
+        for k in ("master", "m", "v", "codes", "scale_inv"):
+            cat = np.concatenate([p[k] for p in parts])
+            assert np.array_equal(cat.view(np.uint8), full[k].view(np.uint8)), (D, k)
+
+
+def test_amax_at_every_position():
+    """16384 tiles; tile k has its largest |value| at element k (sign
+    alternating).  lr = 0 leaves the master unchanged, so the scale must be
+    1/448 in every tile, the code there 0x7E / 0xFE, and every code must
+    match the oracle on a sample of tiles."""
+    n = 16384
+    _say("amax at every position:", n, "tiles, seed 11")
+    rng = np.random.default_rng(11)
+    host = rng.uniform(-0.5, 0.5, (n, 16384)).astype(np.float32)
+    k = np.arange(n)
+    host[k, k] = np.where(k % 2 == 0, 1.0, -1.0).astype(np.float32)
+    dev = torch.from_numpy(host).cuda().view(-1)
+    z = torch.zeros_like(dev)
+    m, v = z.clone(), z.clone()
+    codes = torch.empty(dev.numel(), dtype=torch.uint8, device="cuda")
+    scale = torch.empty(n, dtype=torch.float32, device="cuda")
+    hp = bfz.AdamW(lr=0.0, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1)
+    bfz.adamw_fp8_step(dev, z, m, v, codes, scale, hp)
+    torch.cuda.synchronize()
+    s = scale.cpu().numpy()
+    assert (s == np.float32(1.0) / np.float32(448.0)).all()
+    c = codes.view(n, 16384).cpu().numpy()
+    assert (c[k, k] == np.where(k % 2 == 0, 0x7E, 0xFE)).all()
+    assert np.array_equal(dev.view(n, 16384).cpu().numpy(), host)
+    sample = rng.choice(n, 64, replace=False)
+    oc, osc, _ = oracle.quant_tiles(np.ascontiguousarray(host[sample]).reshape(-1))
+    assert np.array_equal(c[sample].reshape(-1), oc)
+    del dev, z, m, v, codes
+    _free()
+
+
+def test_deterministic_and_empty():
+    w = WL.tiny()
+    _say("determinism + n_tiles=0, tiny")
+    outs = []
+    for _ in range(2):
+        g = GpuWorkload(w)
+        g.load_state()
+        g.run_steps()
+        outs.append(g.tiles(list(range(g.q))))
+    for k in outs[0]:
+        assert np.array_equal(outs[0][k].view(np.uint8), outs[1][k].view(np.uint8)), k
+    before = g.codes.clone()
+    bfz.adamw_fp8_step(g.master, g.grad, g.m, g.v, g.codes, g.scale_inv,
+                       bfz.AdamW(step=4, **WL.HP), n_tiles=0)
+    torch.cuda.synchronize()
+    assert torch.equal(before, g.codes)
+
+
+def test_misaligned_pointer_is_rejected():
+    _say("alignment errors")
+    x = torch.zeros(2 * 16384 + 4, dtype=torch.float32, device="cuda")
+    c = torch.zeros(2 * 16384 + 16, dtype=torch.uint8, device="cuda")
+    s = torch.zeros(2, dtype=torch.float32, device="cuda")
+    off = x[1:1 + 16384]
+    with pytest.raises(bfz.BfzError) as e:
+        bfz.adamw_fp8_step(off, off, off, off, c[:16384], s, bfz.AdamW(step=1, **WL.HP))
+    assert e.value.code == bfz.BFZ_EALIGN
