@@ -8,6 +8,8 @@
 // HIP defaults), so results do not depend on instruction scheduling.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "bfz_internal.h"
 
 #pragma clang fp contract(off)
@@ -15,9 +17,7 @@
 namespace bfz {
 namespace {
 
-constexpr int kThreads = 256;                            // 4 wave64s per tile
-constexpr int kWaves = kThreads / 64;
-constexpr int kStepVec = kTileElems / 4 / kThreads;      // float4 per thread per array
+constexpr int kThreads = 256;  // fold / unfold / encode: 4 wave64s per workgroup
 
 // ---------------------------------------------------------------------
 // E4M3 (OCP E4M3FN) rounding of a binary32 value: nearest value, ties to
@@ -59,50 +59,85 @@ __device__ __forceinline__ void adamw_elem(float& p, float g, float& m, float& v
     p = pp;
 }
 
-__device__ __forceinline__ float abs_max4(float a, const float4& x) {
+// Non-temporal (streaming) 16-byte accesses: every byte of the step is
+// touched exactly once, so keeping it in the caches only evicts the other
+// streams.  The builtins take clang vector types.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 load_stream(const f32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void store_stream(f32x4* p, f32x4 v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_stream(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+
+__device__ __forceinline__ float abs_max4(float a, const f32x4& x) {
     return fmaxf(fmaxf(a, fmaxf(fabsf(x.x), fabsf(x.y))), fmaxf(fabsf(x.z), fabsf(x.w)));
 }
 
-__device__ __forceinline__ uint32_t pack_codes(const float4& x, float scale) {
+__device__ __forceinline__ uint32_t pack_codes(const f32x4& x, float scale) {
     return e4m3_code(x.x / scale) | (e4m3_code(x.y / scale) << 8) |
            (e4m3_code(x.z / scale) << 16) | (e4m3_code(x.w / scale) << 24);
 }
 
-// One workgroup owns one tile.  Pass 1 streams master/grad/m/v in with
-// coalesced 16-byte loads (thread t takes float4 t, t + 256, ...), updates
-// them in registers, writes master/m/v straight back and keeps the new
-// master values in registers.  The tile amax is reduced across the wave by
-// lane shuffles, then across the 4 waves through LDS (one barrier).  Pass 2
-// quantizes the register-held values: 4 codes per thread and float4, one
-// 32-bit store, so HBM sees each input once and each output once.
-__global__ __launch_bounds__(kThreads) void step_kernel(
+// Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD
+// b % 8).  Map them so each XCD walks one contiguous eighth of the tiles:
+// the XCDs then stream from 8 compact address windows instead of all of
+// them interleaving tile by tile.  Bijective for any n_tiles.
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t n_tiles) {
+    const int64_t per = n_tiles / 8, x = b % 8, j = b / 8;
+    return j < per ? x * per + j : 8 * per + x;
+}
+
+// One 1024-thread workgroup (16 wave64s) owns one tile: each thread holds
+// 4 float4 of it.  All 16 of a thread's 16-byte loads (master, grad, m, v)
+// are issued before any arithmetic, so 256 KiB per tile are in flight at
+// once; the update runs in registers, master/m/v go straight back out, and
+// the new master values stay in VGPRs.  The tile amax: lane shuffles within
+// each wave, then the 16 wave maxima through LDS (one barrier).  Then the
+// register-held values are quantized and stored as one 32-bit word of 4
+// codes per float4.  HBM sees each input once and each output once.  The
+// launch reserves enough LDS that one tile is in flight per CU, which keeps
+// the DRAM access windows compact (measured faster than 2-4 tiles per CU).
+constexpr int kStepThreads = 1024;
+constexpr int kStepWaves = kStepThreads / 64;
+constexpr int kStepVec = kTileElems / 4 / kStepThreads;  // float4 per thread per array
+constexpr int kStepLdsBytes = 96 * 1024;                 // > half of the 160 KiB per CU
+
+__global__ __launch_bounds__(kStepThreads) void step_kernel(
     float* __restrict__ master, const float* __restrict__ grad, float* __restrict__ mom1,
     float* __restrict__ mom2, uint32_t* __restrict__ codes, float* __restrict__ scale_inv,
-    StepScalars s) {
-    __shared__ float wave_amax[kWaves];
-    const int64_t tile = blockIdx.x;
+    StepScalars s, int64_t n_tiles) {
+    extern __shared__ float wave_amax[];
+    const int64_t tile = xcd_tile(blockIdx.x, n_tiles);
     const int64_t base = tile * (kTileElems / 4);
-    float4* P = reinterpret_cast<float4*>(master) + base;
-    const float4* G = reinterpret_cast<const float4*>(grad) + base;
-    float4* M = reinterpret_cast<float4*>(mom1) + base;
-    float4* V = reinterpret_cast<float4*>(mom2) + base;
+    f32x4* P = reinterpret_cast<f32x4*>(master) + base;
+    const f32x4* G = reinterpret_cast<const f32x4*>(grad) + base;
+    f32x4* M = reinterpret_cast<f32x4*>(mom1) + base;
+    f32x4* V = reinterpret_cast<f32x4*>(mom2) + base;
 
-    float4 keep[kStepVec];
+    f32x4 p[kStepVec], g[kStepVec], m[kStepVec], v[kStepVec];
+#pragma unroll
+    for (int k = 0; k < kStepVec; ++k) {
+        const int i = k * kStepThreads + threadIdx.x;
+        p[k] = load_stream(P + i);
+        g[k] = load_stream(G + i);
+        m[k] = load_stream(M + i);
+        v[k] = load_stream(V + i);
+    }
     float amax = 0.0f;
 #pragma unroll
     for (int k = 0; k < kStepVec; ++k) {
-        const int i = k * kThreads + threadIdx.x;
-        float4 p = P[i], m = M[i], v = V[i];
-        const float4 g = G[i];
-        adamw_elem(p.x, g.x, m.x, v.x, s);
-        adamw_elem(p.y, g.y, m.y, v.y, s);
-        adamw_elem(p.z, g.z, m.z, v.z, s);
-        adamw_elem(p.w, g.w, m.w, v.w, s);
-        M[i] = m;
-        V[i] = v;
-        P[i] = p;
-        keep[k] = p;
-        amax = abs_max4(amax, p);
+        const int i = k * kStepThreads + threadIdx.x;
+#pragma unroll
+        for (int l = 0; l < 4; ++l) {
+            float pl = p[k][l], ml = m[k][l], vl = v[k][l];
+            adamw_elem(pl, g[k][l], ml, vl, s);
+            p[k][l] = pl;
+            m[k][l] = ml;
+            v[k][l] = vl;
+        }
+        store_stream(M + i, m[k]);
+        store_stream(V + i, v[k]);
+        store_stream(P + i, p[k]);
+        amax = abs_max4(amax, p[k]);
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
@@ -110,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(
     __syncthreads();
     amax = wave_amax[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) amax = fmaxf(amax, wave_amax[w]);
+    for (int w = 1; w < kStepWaves; ++w) amax = fmaxf(amax, wave_amax[w]);
 
     // scale_inv = amax / 448; an all-zero tile takes 1 and codes 0.
     const bool zero = amax == 0.0f;
@@ -118,10 +153,8 @@ __global__ __launch_bounds__(kThreads) void step_kernel(
     if (threadIdx.x == 0) scale_inv[tile] = scale;
     uint32_t* C = codes + base;
 #pragma unroll
-    for (int k = 0; k < kStepVec; ++k) {
-        const int i = k * kThreads + threadIdx.x;
-        C[i] = zero ? 0u : pack_codes(keep[k], scale);
-    }
+    for (int k = 0; k < kStepVec; ++k)
+        store_stream(C + k * kStepThreads + threadIdx.x, zero ? 0u : pack_codes(p[k], scale));
 }
 
 // Fold: one workgroup per slot.  Thread t copies float4 column t % 32 of
@@ -225,9 +258,22 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const float* __restric
 int launch_step(float* master, const float* grad, float* m, float* v, uint8_t* codes,
                 float* scale_inv, int64_t n_tiles, const StepScalars& s, void* stream) {
     if (n_tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(step_kernel, dim3((uint32_t)n_tiles), dim3(kThreads), 0,
+    // The dynamic-LDS limit is a per-device function attribute: set it once
+    // on each device the step runs on.
+    static std::atomic<uint64_t> lds_ready{0};
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    const uint64_t bit = uint64_t(1) << (dev & 63);
+    if (!(lds_ready.load(std::memory_order_acquire) & bit)) {
+        err = hipFuncSetAttribute(reinterpret_cast<const void*>(step_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, kStepLdsBytes);
+        if (err != hipSuccess) return err;
+        lds_ready.fetch_or(bit, std::memory_order_release);
+    }
+    hipLaunchKernelGGL(step_kernel, dim3((uint32_t)n_tiles), dim3(kStepThreads), kStepLdsBytes,
                        (hipStream_t)stream, master, grad, m, v,
-                       reinterpret_cast<uint32_t*>(codes), scale_inv, s);
+                       reinterpret_cast<uint32_t*>(codes), scale_inv, s, n_tiles);
     return hipGetLastError();
 }
 
