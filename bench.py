@@ -1,10 +1,11 @@
 """Benchmark of the block-wise FP8 ZeRO-1 shard step on one MI355X.
 
 One step = the whole per-step path of one rank: fold its row-major FP32
-grads into the tile-major shard (pack_shard), the fused AdamW + per-tile
-E4M3 requantization (adamw_fp8_step), and the unfold of codes and scales
-into row-major FP8 weights plus the scale grid (unpack_fp8).  The split
-itself (the planner) runs once at set-up.
+grads into the tile layout, the AdamW + per-tile E4M3 requantization, and
+the unfold of codes and scales into row-major FP8 weights plus the scale
+grid.  By default the fold is fused into the update (fold_adamw_fp8_step,
+then unpack_fp8); --unfused times pack_shard + adamw_fp8_step + unpack_fp8.
+The split itself (the planner) runs once at set-up.
 
 Default workload: the dense-LLM rank shard -- 32 layers x {4 of 4096x4096,
 2 of 4096x11008, 1 of 11008x4096}, D = 8, rank 0: 49408 tiles, 809.5M
@@ -14,10 +15,11 @@ t = 11 gradients, which stay resident in HBM (inputs are never re-drawn
 inside the timed region).
 
 Output: one JSON line.  value = shard elements per second of the whole
-step.  roofline = the fused step kernel's algorithmic HBM bytes per launch
-(29 B per element + 4 B per tile) over its mean launch time, measured with
-HIP events on the stream the kernels run on.  cpu_baseline = the C oracle
-on a bounded sample of the same workload, on the host's cores.
+step.  roofline = the step kernel's algorithmic HBM bytes per launch
+(29 B per element + 4 B per tile; the gradient read counts valid elements)
+over its mean launch time, measured with HIP events on the stream the
+kernels run on.  cpu_baseline = the C oracle on a bounded sample of the
+same workload, on the host's cores.
 """
 import argparse
 import hashlib
@@ -38,7 +40,10 @@ STEP_BYTES_PER_TILE = 4           # scale_inv
 PACK_BYTES_PER_ELEM = 8           # read grad + write tile
 UNPACK_BYTES_PER_ELEM = 2         # read code + write code
 UNPACK_BYTES_PER_TILE = 8         # read + write scale
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "step_kernel_dense_llm_traffic.md")
+TRAFFIC_FILES = {
+    "fold_step_kernel": os.path.join(ROOT, "profiles", "fold_step_kernel_dense_llm_traffic.md"),
+    "step_kernel": os.path.join(ROOT, "profiles", "step_kernel_dense_llm_traffic.md"),
+}
 KERNEL_SRC = os.path.join(ROOT, "blockwise_fp8_zero_amd", "csrc", "kernels.hip")
 
 
@@ -51,12 +56,13 @@ def kernel_sha():
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(per_launch_algo_bytes):
-    """HBM bytes per launch of the step kernel from the committed rocprofv3
-    PMC summary, if it was taken on the current kernel source; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from its committed rocprofv3 PMC
+    summary, if that was taken on the current kernel source; else None."""
+    path = TRAFFIC_FILES[kernel]
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     sha = re.search(r"kernel_sha256:\s*([0-9a-f]{64})", text)
     tb = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not sha or not tb or sha.group(1) != kernel_sha():
@@ -141,6 +147,9 @@ def main():
     ap.add_argument("--workload", default="dense_llm",
                     choices=["dense_llm", "ragged", "moe_experts", "large", "tiny"])
     ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time pack_shard + adamw_fp8_step + unpack_fp8 instead of "
+                         "fold_adamw_fp8_step + unpack_fp8")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -157,7 +166,7 @@ def main():
     w = WL.BY_NAME[args.workload]()
     log(f"workload {w.name}: {w.description}")
     t0 = time.perf_counter()
-    g = GpuWorkload(w)
+    g = GpuWorkload(w, fused=not args.unfused)
     g.load_state()
     prior = w.steps[:-1]
     if prior:
@@ -177,10 +186,14 @@ def main():
     t_next = w.measured_step
 
     def one_step(t, ev=None):
-        g.pack_grads()
+        if args.unfused:
+            g.pack_grads()
         if ev is not None:
             ev[0].record(stream)
-        g.step(t)
+        if args.unfused:
+            g.step(t)
+        else:
+            g.fold_step(t)
         if ev is not None:
             ev[1].record(stream)
         g.unpack(fp8, sc)
@@ -206,13 +219,16 @@ def main():
     ms_per_step = total_ms / args.steps
 
     elems = g.q * bfz.TILE_ELEMS
-    valid = sum(min(128, int(r[4])) * min(128, int(r[5])) for r in g.table[:g.owned]) \
-        if w.name == "ragged" else g.owned * bfz.TILE_ELEMS
-    algo_bytes = STEP_BYTES_PER_ELEM * elems + STEP_BYTES_PER_TILE * g.q
+    valid = int((g.table[:g.owned, 4] * g.table[:g.owned, 5]).sum())
+    kernel = "step_kernel" if args.unfused else "fold_step_kernel"
+    # the fused kernel reads the gradient of valid elements only
+    grad_elems = elems if args.unfused else valid
+    algo_bytes = (STEP_BYTES_PER_ELEM - 4) * elems + 4 * grad_elems + STEP_BYTES_PER_TILE * g.q
     achieved = algo_bytes / (step_kernel_ms * 1e-3) / 1e9
-    whole_bytes = algo_bytes + PACK_BYTES_PER_ELEM * elems + \
-        UNPACK_BYTES_PER_ELEM * elems + UNPACK_BYTES_PER_TILE * g.q
-    traffic = measured_traffic(algo_bytes) if w.name == "dense_llm" else None
+    whole_bytes = algo_bytes + UNPACK_BYTES_PER_ELEM * elems + UNPACK_BYTES_PER_TILE * g.q
+    if args.unfused:
+        whole_bytes += PACK_BYTES_PER_ELEM * elems
+    traffic = measured_traffic(kernel) if w.name == "dense_llm" else None
 
     out = {
         "metric": METRIC,
@@ -235,14 +251,15 @@ def main():
             "D": w.D,
             "rank": w.rank,
             "first_timed_step_t": w.measured_step + args.warmup,
-            "step_path": "pack_shard(grad) + adamw_fp8_step + unpack_fp8",
+            "step_path": ("pack_shard(grad) + adamw_fp8_step + unpack_fp8" if args.unfused
+                          else "fold_adamw_fp8_step + unpack_fp8"),
         },
         "step_hbm_GBps": whole_bytes / (ms_per_step * 1e-3) / 1e9,
         "step_hbm_frac": whole_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "adamw_fp8_step_ms": step_kernel_ms,
-        "adamw_fp8_step_elems_per_s": elems / (step_kernel_ms * 1e-3),
+        "step_kernel_ms": step_kernel_ms,
+        "step_kernel_elems_per_s": elems / (step_kernel_ms * 1e-3),
         "roofline": {
-            "kernel": "adamw_fp8_step (step_kernel)",
+            "kernel": kernel,
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,

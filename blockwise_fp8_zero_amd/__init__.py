@@ -53,6 +53,7 @@ def lib():
         L.bfz_plan_tile.argtypes = [P, i64, P]
         L.pack_shard.argtypes = [P, P, P, P]
         L.adamw_fp8_step.argtypes = [P, P, P, P, P, P, i64, C.POINTER(AdamW), P]
+        L.fold_adamw_fp8_step.argtypes = [P, P, P, P, P, P, P, C.POINTER(AdamW), P]
         L.unpack_fp8.argtypes = [P, P, P, P, P, P]
         L.bfz_e4m3_encode.argtypes = [P, P, i64, P]
         L.bfz_last_error.argtypes = []
@@ -176,6 +177,22 @@ def adamw_fp8_step(master, grad, m, v, codes, scale_inv, hp, n_tiles=None, strea
             _dev(m, torch.float32, "m", n), _dev(v, torch.float32, "v", n),
             _dev(codes, torch.uint8, "codes", n), _dev(scale_inv, torch.float32, "scale_inv", n_tiles)]
     _check(lib().adamw_fp8_step(*args, n_tiles, C.byref(hp), _stream(stream)))
+
+
+def fold_adamw_fp8_step(plan: Plan, grads, master, m, v, codes, scale_inv, hp, stream=None):
+    """pack_shard of the row-major gradients grads[p] and adamw_fp8_step over
+    the whole shard in one pass (the folded gradient is never stored)."""
+    import torch
+    if isinstance(hp, dict):
+        hp = AdamW(**hp)
+    arr = _ptr_array(grads, torch.float32, "grads", len(plan.dims))
+    q = plan.shard_tiles
+    n = q * TILE_ELEMS
+    args = [_dev(master, torch.float32, "master", n), _dev(m, torch.float32, "m", n),
+            _dev(v, torch.float32, "v", n), _dev(codes, torch.uint8, "codes", n),
+            _dev(scale_inv, torch.float32, "scale_inv", q)]
+    _check(lib().fold_adamw_fp8_step(plan.handle, C.cast(arr, C.c_void_p), *args, C.byref(hp),
+                                     _stream(stream)))
 
 
 def unpack_fp8(plan: Plan, codes, scale_inv, dst_fp8, dst_scale, stream=None):

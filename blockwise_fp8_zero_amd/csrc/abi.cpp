@@ -92,6 +92,40 @@ extern "C" int unpack_fp8(const bfz_plan* plan, const uint8_t* codes, const floa
     return BFZ_OK;
 }
 
+namespace {
+
+// The step's scalars, formed in double and rounded to binary32 once each:
+// the bias corrections 1 - beta^t enter as lr / (1 - beta1^t) and
+// sqrt(1 - beta2^t), as in the Int8AdamW step (lpnh.cn essay, section 4.3).
+int make_scalars(const bfz_adamw* hp, StepScalars* s, const char* where) {
+    const double lr = hp->lr, b1 = hp->beta1, b2 = hp->beta2, eps = hp->eps, wd = hp->weight_decay;
+    if (!std::isfinite(lr) || !std::isfinite(eps) || !std::isfinite(wd) || !(eps >= 0.0) ||
+        !(b1 >= 0.0 && b1 < 1.0) || !(b2 >= 0.0 && b2 < 1.0) || hp->step < 1)
+        return fail(BFZ_EINVAL,
+                    "%s: need finite lr/eps/weight_decay, eps >= 0, 0 <= beta < 1, step >= 1", where);
+    const double t = double(hp->step);
+    s->b1 = float(b1);
+    s->c1 = float(1.0 - b1);
+    s->b2 = float(b2);
+    s->c2 = float(1.0 - b2);
+    s->step_size = float(lr / (1.0 - std::pow(b1, t)));
+    s->sbc2 = float(std::sqrt(1.0 - std::pow(b2, t)));
+    s->eps = float(eps);
+    s->decay = float(lr * wd);
+    s->has_decay = wd != 0.0;
+    return BFZ_OK;
+}
+
+int check_state(float* master, float* m, float* v, uint8_t* codes, float* scale_inv,
+                const char* where) {
+    if (!aligned(master, 16) || !aligned(m, 16) || !aligned(v, 16) || !aligned(codes, 16))
+        return fail(BFZ_EALIGN, "%s: master, grad, m, v and codes must be 16-byte aligned", where);
+    if (!aligned(scale_inv, 4)) return fail(BFZ_EALIGN, "%s: scale_inv must be 4-byte aligned", where);
+    return BFZ_OK;
+}
+
+}  // namespace
+
 extern "C" int adamw_fp8_step(float* master, const float* grad, float* m, float* v,
                               uint8_t* codes, float* scale_inv, int64_t n_tiles,
                               const bfz_adamw* hp, void* stream) {
@@ -99,32 +133,43 @@ extern "C" int adamw_fp8_step(float* master, const float* grad, float* m, float*
         return fail(BFZ_EINVAL, "adamw_fp8_step: null pointer");
     if (n_tiles < 0 || n_tiles > 0x7FFFFFFF)
         return fail(BFZ_EINVAL, "adamw_fp8_step: n_tiles %lld outside [0, 2^31)", (long long)n_tiles);
-    if (!aligned(master, 16) || !aligned(grad, 16) || !aligned(m, 16) || !aligned(v, 16) ||
-        !aligned(codes, 16))
+    if (!aligned(grad, 16))
         return fail(BFZ_EALIGN, "adamw_fp8_step: master, grad, m, v and codes must be 16-byte aligned");
-    if (!aligned(scale_inv, 4)) return fail(BFZ_EALIGN, "adamw_fp8_step: scale_inv must be 4-byte aligned");
-    const double lr = hp->lr, b1 = hp->beta1, b2 = hp->beta2, eps = hp->eps, wd = hp->weight_decay;
-    if (!std::isfinite(lr) || !std::isfinite(eps) || !std::isfinite(wd) || !(eps >= 0.0) ||
-        !(b1 >= 0.0 && b1 < 1.0) || !(b2 >= 0.0 && b2 < 1.0) || hp->step < 1)
-        return fail(BFZ_EINVAL,
-                    "adamw_fp8_step: need finite lr/eps/weight_decay, eps >= 0, 0 <= beta < 1, step >= 1");
-    // The step's scalars, formed in double and rounded to binary32 once
-    // each: the bias corrections 1 - beta^t enter as lr / (1 - beta1^t)
-    // and sqrt(1 - beta2^t), as in the Int8AdamW step (lpnh.cn essay,
-    // section 4.3).
-    const double t = double(hp->step);
+    int rc = check_state(master, m, v, codes, scale_inv, "adamw_fp8_step");
+    if (rc) return rc;
     StepScalars s;
-    s.b1 = float(b1);
-    s.c1 = float(1.0 - b1);
-    s.b2 = float(b2);
-    s.c2 = float(1.0 - b2);
-    s.step_size = float(lr / (1.0 - std::pow(b1, t)));
-    s.sbc2 = float(std::sqrt(1.0 - std::pow(b2, t)));
-    s.eps = float(eps);
-    s.decay = float(lr * wd);
-    s.has_decay = wd != 0.0;
+    rc = make_scalars(hp, &s, "adamw_fp8_step");
+    if (rc) return rc;
     int err = launch_step(master, grad, m, v, codes, scale_inv, n_tiles, s, stream);
     if (err != hipSuccess) return hip_fail("adamw_fp8_step", err);
+    return BFZ_OK;
+}
+
+extern "C" int fold_adamw_fp8_step(const bfz_plan* plan, const float* const* grad, float* master,
+                                   float* m, float* v, uint8_t* codes, float* scale_inv,
+                                   const bfz_adamw* hp, void* stream) {
+    if (!plan || !grad || !master || !m || !v || !codes || !scale_inv || !hp)
+        return fail(BFZ_EINVAL, "fold_adamw_fp8_step: null pointer");
+    if (!plan->d_entries)
+        return fail(BFZ_ESTATE, "fold_adamw_fp8_step: plan not uploaded (bfz_plan_upload)");
+    int rc = check_weights(plan, reinterpret_cast<const void* const*>(grad), "fold_adamw_fp8_step");
+    if (rc) return rc;
+    for (int32_t w = 0; w < plan->n_weights; ++w)
+        if (grad[w] && !aligned(grad[w], 4))
+            return fail(BFZ_EALIGN, "fold_adamw_fp8_step: gradient %d must be 4-byte aligned", w);
+    rc = check_state(master, m, v, codes, scale_inv, "fold_adamw_fp8_step");
+    if (rc) return rc;
+    StepScalars s;
+    rc = make_scalars(hp, &s, "fold_adamw_fp8_step");
+    if (rc) return rc;
+    for (const Segment& seg : plan->segments) {
+        PackArgs args{};
+        for (int32_t k = 0; k < seg.n_weights; ++k) args.src[k] = grad[seg.weight0 + k];
+        const int64_t off = seg.slot0 * kTileElems;
+        int err = launch_fold_step(plan->d_entries + seg.slot0, seg.n_slots, args, master + off,
+                                   m + off, v + off, codes + off, scale_inv + seg.slot0, s, stream);
+        if (err != hipSuccess) return hip_fail("fold_adamw_fp8_step", err);
+    }
     return BFZ_OK;
 }
 

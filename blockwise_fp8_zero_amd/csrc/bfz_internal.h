@@ -56,6 +56,9 @@ int launch_unpack(const TileEntry* d_entries, int64_t n_slots, const uint8_t* co
                   const float* scale_inv, const UnpackArgs& args, void* stream);
 int launch_step(float* master, const float* grad, float* m, float* v, uint8_t* codes,
                 float* scale_inv, int64_t n_tiles, const StepScalars& s, void* stream);
+int launch_fold_step(const TileEntry* d_entries, int64_t n_slots, const PackArgs& grads,
+                     float* master, float* m, float* v, uint8_t* codes, float* scale_inv,
+                     const StepScalars& s, void* stream);
 int launch_encode(const float* in, uint8_t* out, int64_t n, void* stream);
 const char* hip_error_string(int err);
 

@@ -87,29 +87,60 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t n_tiles) {
 }
 
 // One 1024-thread workgroup (16 wave64s) owns one tile: each thread holds
-// 4 float4 of it.  All 16 of a thread's 16-byte loads (master, grad, m, v)
-// are issued before any arithmetic, so 256 KiB per tile are in flight at
-// once; the update runs in registers, master/m/v go straight back out, and
-// the new master values stay in VGPRs.  The tile amax: lane shuffles within
-// each wave, then the 16 wave maxima through LDS (one barrier).  Then the
-// register-held values are quantized and stored as one 32-bit word of 4
-// codes per float4.  HBM sees each input once and each output once.  The
-// launch reserves enough LDS that one tile is in flight per CU, which keeps
-// the DRAM access windows compact (measured faster than 2-4 tiles per CU).
+// 4 float4 of it (float4 i = k * 1024 + thread, k < 4, i.e. rows
+// 32 k + thread / 32, columns 4 (thread % 32) .. +3).  All 16 of a thread's
+// 16-byte loads (master, grad, m, v) are issued before any arithmetic, so
+// 256 KiB per tile are in flight at once; the update runs in registers,
+// master/m/v go straight back out, and the new master values stay in VGPRs.
+// The tile amax: lane shuffles within each wave, then the 16 wave maxima
+// through LDS (one barrier).  Then the register-held values are quantized
+// and stored as one 32-bit word of 4 codes per float4.  HBM sees each input
+// once and each output once.  The launch reserves enough LDS that one tile
+// is in flight per CU, which keeps the DRAM access windows compact
+// (measured faster than 2-4 tiles per CU).
 constexpr int kStepThreads = 1024;
 constexpr int kStepWaves = kStepThreads / 64;
 constexpr int kStepVec = kTileElems / 4 / kStepThreads;  // float4 per thread per array
 constexpr int kStepLdsBytes = 96 * 1024;                 // > half of the 160 KiB per CU
 
-__global__ __launch_bounds__(kStepThreads) void step_kernel(
-    float* __restrict__ master, const float* __restrict__ grad, float* __restrict__ mom1,
-    float* __restrict__ mom2, uint32_t* __restrict__ codes, float* __restrict__ scale_inv,
-    StepScalars s, int64_t n_tiles) {
-    extern __shared__ float wave_amax[];
-    const int64_t tile = xcd_tile(blockIdx.x, n_tiles);
+// Gradient of a tile already folded into the tile-major shard.
+struct TileMajorGrad {
+    const f32x4* tile;
+    __device__ __forceinline__ f32x4 operator()(int k) const {
+        return load_stream(tile + k * kStepThreads + threadIdx.x);
+    }
+};
+
+// Gradient read straight from the weight's row-major tensor (the fold done
+// on the fly): row 32 k + thread / 32, four columns from 4 (thread % 32).
+// Outside the weight's edge, and in padding slots (origin == nullptr), the
+// gradient is +0.0 -- exactly what the fold would have stored there.
+struct RowMajorGrad {
+    const float* origin;  // the tile's element (0, 0) in its weight
+    int32_t ld;
+    int16_t rows, cols;
+    bool vec;             // W % 4 == 0 and the weight is 16-byte aligned
+    __device__ __forceinline__ f32x4 operator()(int k) const {
+        const int r = k * 32 + (threadIdx.x >> 5), c = 4 * (threadIdx.x & 31);
+        f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (origin == nullptr || r >= rows) return x;
+        const float* q = origin + (int64_t)r * ld + c;
+        if (vec && c + 4 <= cols) return load_stream(reinterpret_cast<const f32x4*>(q));
+#pragma unroll
+        for (int l = 0; l < 4; ++l)
+            if (c + l < cols) x[l] = q[l];
+        return x;
+    }
+};
+
+template <class GradFn>
+__device__ __forceinline__ void step_tile(int64_t tile, float* __restrict__ master,
+                                          float* __restrict__ mom1, float* __restrict__ mom2,
+                                          uint32_t* __restrict__ codes,
+                                          float* __restrict__ scale_inv, const StepScalars& s,
+                                          const GradFn& grad_at, float* wave_amax) {
     const int64_t base = tile * (kTileElems / 4);
     f32x4* P = reinterpret_cast<f32x4*>(master) + base;
-    const f32x4* G = reinterpret_cast<const f32x4*>(grad) + base;
     f32x4* M = reinterpret_cast<f32x4*>(mom1) + base;
     f32x4* V = reinterpret_cast<f32x4*>(mom2) + base;
 
@@ -118,7 +149,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(
     for (int k = 0; k < kStepVec; ++k) {
         const int i = k * kStepThreads + threadIdx.x;
         p[k] = load_stream(P + i);
-        g[k] = load_stream(G + i);
+        g[k] = grad_at(k);
         m[k] = load_stream(M + i);
         v[k] = load_stream(V + i);
     }
@@ -155,6 +186,35 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(
 #pragma unroll
     for (int k = 0; k < kStepVec; ++k)
         store_stream(C + k * kStepThreads + threadIdx.x, zero ? 0u : pack_codes(p[k], scale));
+}
+
+__global__ __launch_bounds__(kStepThreads) void step_kernel(
+    float* __restrict__ master, const float* __restrict__ grad, float* __restrict__ mom1,
+    float* __restrict__ mom2, uint32_t* __restrict__ codes, float* __restrict__ scale_inv,
+    StepScalars s, int64_t n_tiles) {
+    extern __shared__ float wave_amax[];
+    const int64_t tile = xcd_tile(blockIdx.x, n_tiles);
+    const TileMajorGrad g{reinterpret_cast<const f32x4*>(grad) + tile * (kTileElems / 4)};
+    step_tile(tile, master, mom1, mom2, codes, scale_inv, s, g, wave_amax);
+}
+
+// The same step, with the gradient fold fused in: slot s of this launch
+// reads its gradient from the row-major weight its table entry names.
+// master/m/v/codes/scale_inv and entries point at the launch's first slot.
+__global__ __launch_bounds__(kStepThreads) void fold_step_kernel(
+    const TileEntry* __restrict__ entries, PackArgs grads, float* __restrict__ master,
+    float* __restrict__ mom1, float* __restrict__ mom2, uint32_t* __restrict__ codes,
+    float* __restrict__ scale_inv, StepScalars s, int64_t n_slots) {
+    extern __shared__ float wave_amax[];
+    const int64_t slot = xcd_tile(blockIdx.x, n_slots);
+    const TileEntry t = entries[slot];
+    RowMajorGrad g{nullptr, t.ld, t.valid_rows, t.valid_cols, false};
+    if (t.local >= 0) {
+        const float* w = grads.src[t.local];
+        g.origin = w + t.base;
+        g.vec = ((t.ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(w) & 15u) == 0);
+    }
+    step_tile(slot, master, mom1, mom2, codes, scale_inv, s, g, wave_amax);
 }
 
 // Fold: one workgroup per slot.  Thread t copies float4 column t % 32 of
@@ -255,25 +315,47 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const float* __restric
 
 }  // namespace
 
-int launch_step(float* master, const float* grad, float* m, float* v, uint8_t* codes,
-                float* scale_inv, int64_t n_tiles, const StepScalars& s, void* stream) {
-    if (n_tiles == 0) return hipSuccess;
-    // The dynamic-LDS limit is a per-device function attribute: set it once
-    // on each device the step runs on.
-    static std::atomic<uint64_t> lds_ready{0};
+namespace {
+
+// The dynamic-LDS limit is a per-device function attribute: set it once per
+// kernel on each device the step runs on.
+hipError_t reserve_lds(const void* kernel, std::atomic<uint64_t>& ready) {
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
     const uint64_t bit = uint64_t(1) << (dev & 63);
-    if (!(lds_ready.load(std::memory_order_acquire) & bit)) {
-        err = hipFuncSetAttribute(reinterpret_cast<const void*>(step_kernel),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, kStepLdsBytes);
+    if (!(ready.load(std::memory_order_acquire) & bit)) {
+        err = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kStepLdsBytes);
         if (err != hipSuccess) return err;
-        lds_ready.fetch_or(bit, std::memory_order_release);
+        ready.fetch_or(bit, std::memory_order_release);
     }
+    return hipSuccess;
+}
+
+std::atomic<uint64_t> g_step_lds{0}, g_fold_step_lds{0};
+
+}  // namespace
+
+int launch_step(float* master, const float* grad, float* m, float* v, uint8_t* codes,
+                float* scale_inv, int64_t n_tiles, const StepScalars& s, void* stream) {
+    if (n_tiles == 0) return hipSuccess;
+    hipError_t err = reserve_lds(reinterpret_cast<const void*>(step_kernel), g_step_lds);
+    if (err != hipSuccess) return err;
     hipLaunchKernelGGL(step_kernel, dim3((uint32_t)n_tiles), dim3(kStepThreads), kStepLdsBytes,
                        (hipStream_t)stream, master, grad, m, v,
                        reinterpret_cast<uint32_t*>(codes), scale_inv, s, n_tiles);
+    return hipGetLastError();
+}
+
+int launch_fold_step(const TileEntry* d_entries, int64_t n_slots, const PackArgs& grads,
+                     float* master, float* m, float* v, uint8_t* codes, float* scale_inv,
+                     const StepScalars& s, void* stream) {
+    if (n_slots == 0) return hipSuccess;
+    hipError_t err = reserve_lds(reinterpret_cast<const void*>(fold_step_kernel), g_fold_step_lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(fold_step_kernel, dim3((uint32_t)n_slots), dim3(kStepThreads),
+                       kStepLdsBytes, (hipStream_t)stream, d_entries, grads, master, m, v,
+                       reinterpret_cast<uint32_t*>(codes), scale_inv, s, n_slots);
     return hipGetLastError();
 }
 

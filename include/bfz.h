@@ -15,6 +15,8 @@
  *   3. unfolds the codes and scales back to row-major FP8 weights and the
  *      row-major scale grid (unpack_fp8; the unfold of "Parameter layout
  *      transform" and "Summary").
+ * fold_adamw_fp8_step does 1 and 2 in one pass, reading the gradients
+ * straight from their row-major weights.
  *
  * Conventions shared by every call:
  *   - A tile is 16384 contiguous elements: 128 rows of 128, row-major.
@@ -22,9 +24,9 @@
  *   - Device pointers are caller-owned (the library never frees them); the
  *     library allocates only the plan's small device table, in
  *     bfz_plan_upload, freed by bfz_plan_destroy.
- *   - pack_shard, adamw_fp8_step and unpack_fp8 are asynchronous on the HIP
- *     stream passed as `stream` (NULL = the null stream): they only enqueue
- *     kernels, never allocate, never synchronize.
+ *   - pack_shard, adamw_fp8_step, fold_adamw_fp8_step and unpack_fp8 are
+ *     asynchronous on the HIP stream passed as `stream` (NULL = the null
+ *     stream): they only enqueue kernels, never allocate, never synchronize.
  *   - Return value: 0 on success, else a negative BFZ_E* code; the message
  *     for the calling thread's last failure is bfz_last_error().
  *   - Non-finite inputs (NaN, Inf) give unspecified results.
@@ -140,6 +142,26 @@ int pack_shard(const bfz_plan* plan, const float* const* src, float* dst, void* 
  */
 int adamw_fp8_step(float* master, const float* grad, float* m, float* v, uint8_t* codes,
                    float* scale_inv, int64_t n_tiles, const bfz_adamw* hp, void* stream);
+
+/*
+ * pack_shard of the gradients and adamw_fp8_step in one pass: the same
+ * result, bit for bit, as
+ *     pack_shard(plan, grad, tmp, stream);
+ *     adamw_fp8_step(master, tmp, m, v, codes, scale_inv, q, hp, stream);
+ * but each gradient element is read once from its row-major weight and the
+ * folded copy is never written (the fold of the reduced gradients,
+ * "Parameter layout transform" and "Summary", done inside the update).
+ * grad: host array of n_params device pointers to the row-major FP32
+ * gradients (NULL allowed for weights the rank does not touch; 4-byte
+ * alignment is enough, a 16-byte aligned weight whose W is a multiple of 4
+ * takes the vector path).  master, m, v: q * 16384 floats in the shard
+ * layout, updated in place; codes: q * 16384 bytes; scale_inv: q floats.
+ * Padding slots must hold zero state; their gradient is taken as zero.
+ * Errors: BFZ_EINVAL, BFZ_EALIGN, BFZ_ESTATE, BFZ_EHIP.
+ */
+int fold_adamw_fp8_step(const bfz_plan* plan, const float* const* grad, float* master, float* m,
+                        float* v, uint8_t* codes, float* scale_inv, const bfz_adamw* hp,
+                        void* stream);
 
 /*
  * Unfold of the rank's owned slots: dst_fp8[p][e][128 i + a][128 j + b] =

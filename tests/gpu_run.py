@@ -21,8 +21,11 @@ def hp_for(w, t):
 class GpuWorkload:
     """Device state of one rank's shard of workload w."""
 
-    def __init__(self, w: WL.Workload, device="cuda"):
+    def __init__(self, w: WL.Workload, device="cuda", fused=False):
+        """fused: take each step with fold_adamw_fp8_step (gradients read
+        row-major) instead of pack_shard + adamw_fp8_step."""
         self.w = w
+        self.fused = fused
         self.device = torch.device(device)
         with torch.cuda.device(self.device):
             self.plan = bfz.Plan(w.dims, w.D, w.rank)
@@ -74,12 +77,23 @@ class GpuWorkload:
         bfz.adamw_fp8_step(self.master, self.grad, self.m, self.v, self.codes, self.scale_inv,
                            hp_for(self.w, t))
 
+    def fold_step(self, t):
+        bfz.fold_adamw_fp8_step(self.plan, self.grad_rm, self.master, self.m, self.v, self.codes,
+                                self.scale_inv, hp_for(self.w, t))
+
+    def apply(self, t):
+        """One step on the current row-major gradients."""
+        if self.fused:
+            self.fold_step(t)
+        else:
+            self.pack_grads()
+            self.step(t)
+
     def run_steps(self, steps=None):
         """Draw, fold and apply the grads of each step counter in `steps`."""
         for t in (steps if steps is not None else self.w.steps):
             self.draw_grads(t)
-            self.pack_grads()
-            self.step(t)
+            self.apply(t)
             self.t_done = t
         torch.cuda.synchronize(self.device)
 

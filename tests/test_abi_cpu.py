@@ -103,6 +103,13 @@ def test_pack_unpack_errors_without_gpu():
     d8 = (C.c_void_p * 2)(0x10000, 0x20000)
     assert L.unpack_fp8(p.handle, C.c_void_p(0x40000), C.c_void_p(0x50000), C.cast(d8, C.c_void_p),
                         C.cast(d8, C.c_void_p), None) == bfz.BFZ_ESTATE
+    hp = bfz.AdamW(lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1)
+    st = [C.c_void_p(x) for x in (0x40000, 0x50000, 0x60000, 0x70000, 0x80000)]
+    assert L.fold_adamw_fp8_step(p.handle, C.cast(src, C.c_void_p), *st, C.byref(hp),
+                                 None) == bfz.BFZ_ESTATE
+    assert L.fold_adamw_fp8_step(p.handle, None, *st, C.byref(hp), None) == bfz.BFZ_EINVAL
+    assert L.fold_adamw_fp8_step(None, C.cast(src, C.c_void_p), *st, C.byref(hp),
+                                 None) == bfz.BFZ_EINVAL
     assert L.bfz_e4m3_encode(None, C.c_void_p(0x10), 5, None) == bfz.BFZ_EINVAL
     assert L.bfz_e4m3_encode(C.c_void_p(0x10), C.c_void_p(0x10), -1, None) == bfz.BFZ_EINVAL
     assert L.bfz_plan_tile(p.handle, 99, C.cast((C.c_int64 * 6)(), C.c_void_p)) == bfz.BFZ_EINVAL

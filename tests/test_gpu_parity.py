@@ -41,10 +41,14 @@ def _check(gpu, ora, what):
     return rep
 
 
-def test_tiny_every_step_every_slot():
+MODES = ["pack+step", "fused"]
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_tiny_every_step_every_slot(mode):
     w = WL.tiny()
-    _say("tiny: 256x384, 3 steps, seed", w.seed)
-    g = GpuWorkload(w)
+    _say("tiny: 256x384, 3 steps, seed", w.seed, "mode", mode)
+    g = GpuWorkload(w, fused=mode == "fused")
     g.load_state()
     slots = list(range(g.q))
     for k, t in enumerate(w.steps):
@@ -64,10 +68,11 @@ def test_tiny_every_step_every_slot():
     assert np.array_equal(sc[0].cpu().numpy().reshape(E, 2, 3), osc)
 
 
-def test_ragged_every_slot():
+@pytest.mark.parametrize("mode", MODES)
+def test_ragged_every_slot(mode):
     w = WL.ragged()
-    _say("ragged: 40 matrices, D=8 rank 3, seed", w.seed)
-    g = GpuWorkload(w)
+    _say("ragged: 40 matrices, D=8 rank 3, seed", w.seed, "mode", mode)
+    g = GpuWorkload(w, fused=mode == "fused")
     g.load_state()
     g.run_steps()
     slots = list(range(g.q))
@@ -92,11 +97,13 @@ def test_ragged_every_slot():
     _free()
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("name", ["dense_llm", "moe_experts", "large"])
-def test_full_size_sampled(name):
+def test_full_size_sampled(name, mode):
     w = WL.BY_NAME[name]()
-    _say(name, "full size,", len(w.dims), "weights, D =", w.D, "rank", w.rank, "seed", w.seed)
-    g = GpuWorkload(w)
+    _say(name, "full size,", len(w.dims), "weights, D =", w.D, "rank", w.rank, "seed", w.seed,
+         "mode", mode)
+    g = GpuWorkload(w, fused=mode == "fused")
     g.load_state()
     g.run_steps()
     slots = sample_slots(w)
@@ -127,14 +134,15 @@ def test_full_size_sampled(name):
     _free()
 
 
-def test_rank_decomposition_is_invariant():
+@pytest.mark.parametrize("mode", MODES)
+def test_rank_decomposition_is_invariant(mode):
     """Every tile's result is independent of which rank owns it: the union
     of the D shards equals the single-rank run, bit for bit."""
     w1 = WL.ragged()
     w1.dims = w1.dims[:6]
     w1.D, w1.rank = 1, 0
-    _say("rank invariance: 6 ragged matrices, D in {1, 3, 7}")
-    ref = GpuWorkload(w1)
+    _say("rank invariance: 6 ragged matrices, D in {1, 3, 7}, mode", mode)
+    ref = GpuWorkload(w1, fused=mode == "fused")
     ref.load_state()
     ref.run_steps()
     full = ref.tiles(list(range(ref.owned)))
@@ -143,7 +151,7 @@ def test_rank_decomposition_is_invariant():
         for r in range(D):
             w = WL.ragged()
             w.dims, w.D, w.rank = w1.dims, D, r
-            g = GpuWorkload(w)
+            g = GpuWorkload(w, fused=mode == "fused")
             g.load_state()
             g.run_steps()
             if g.owned:
@@ -205,6 +213,42 @@ def test_deterministic_and_empty():
                        bfz.AdamW(step=4, **WL.HP), n_tiles=0)
     torch.cuda.synchronize()
     assert torch.equal(before, g.codes)
+
+
+def test_fused_equals_unfused_on_misaligned_gradients():
+    """Gradients that start 4 bytes into their buffer (no 16-byte vector
+    path) give the same bits through both routes."""
+    dims = [(1, 300, 260), (2, 129, 516), (1, 128, 128)]
+    _say("fused vs pack+step, misaligned gradients, seed 21")
+    rng = np.random.default_rng(21)
+    plan = bfz.Plan(dims, 2, 1)
+    q = plan.shard_tiles
+    n = q * 16384
+    state0 = [torch.from_numpy(rng.normal(0, s, n).astype(np.float32)).cuda()
+              for s in (0.02, 1e-4, 1e-7)]
+    for x in state0:  # padding slots hold zero state
+        x.view(q, 16384)[plan.owned_tiles:] = 0
+    state0[2].abs_()
+    grads = []
+    for d in dims:
+        raw = torch.from_numpy(rng.normal(0, 1e-3, int(np.prod(d)) + 1).astype(np.float32)).cuda()
+        grads.append(raw[1:])
+    outs = []
+    for fused in (False, True):
+        p, m, v = (x.clone() for x in state0)
+        codes = torch.empty(n, dtype=torch.uint8, device="cuda")
+        sc = torch.empty(q, dtype=torch.float32, device="cuda")
+        hp = bfz.AdamW(step=5, **WL.HP)
+        if fused:
+            bfz.fold_adamw_fp8_step(plan, grads, p, m, v, codes, sc, hp)
+        else:
+            gt = torch.empty(n, dtype=torch.float32, device="cuda")
+            bfz.pack_shard(plan, grads, gt)
+            bfz.adamw_fp8_step(p, gt, m, v, codes, sc, hp)
+        torch.cuda.synchronize()
+        outs.append([x.cpu().numpy() for x in (p, m, v, codes, sc)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
 def test_misaligned_pointer_is_rejected():
