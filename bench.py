@@ -3,8 +3,12 @@
 One step = the whole per-step path of one rank: fold its row-major FP32
 grads into the tile layout, the AdamW + per-tile E4M3 requantization, and
 the unfold of codes and scales into row-major FP8 weights plus the scale
-grid.  By default the fold is fused into the update (fold_adamw_fp8_step,
-then unpack_fp8); --unfused times pack_shard + adamw_fp8_step + unpack_fp8.
+grid.  --path picks how:
+  fused_unpack (default): fold_adamw_fp8_step_unpack -- all of it in one
+      kernel, writing the tile-major codes/scales (the all-gather payload)
+      and the row-major FP8 weights/scale grids;
+  fused:   fold_adamw_fp8_step, then unpack_fp8;
+  unfused: pack_shard, adamw_fp8_step, unpack_fp8.
 The split itself (the planner) runs once at set-up.
 
 Default workload: the dense-LLM rank shard -- 32 layers x {4 of 4096x4096,
@@ -16,9 +20,10 @@ inside the timed region).
 
 Output: one JSON line.  value = shard elements per second of the whole
 step.  roofline = the step kernel's algorithmic HBM bytes per launch
-(29 B per element + 4 B per tile; the gradient read counts valid elements)
-over its mean launch time, measured with HIP events on the stream the
-kernels run on.  cpu_baseline = the C oracle on a bounded sample of the
+(29 B per element + 4 B per tile, plus 1 B per element + 4 B per tile for
+the row-major codes and scales in the one-kernel path; gradient reads and
+row-major writes count valid elements) over its mean launch time, measured
+with HIP events on the stream the kernels run on.  cpu_baseline = the C oracle on a bounded sample of the
 same workload, on the host's cores.
 """
 import argparse
@@ -40,10 +45,10 @@ STEP_BYTES_PER_TILE = 4           # scale_inv
 PACK_BYTES_PER_ELEM = 8           # read grad + write tile
 UNPACK_BYTES_PER_ELEM = 2         # read code + write code
 UNPACK_BYTES_PER_TILE = 8         # read + write scale
-TRAFFIC_FILES = {
-    "fold_step_kernel": os.path.join(ROOT, "profiles", "fold_step_kernel_dense_llm_traffic.md"),
-    "step_kernel": os.path.join(ROOT, "profiles", "step_kernel_dense_llm_traffic.md"),
-}
+TRAFFIC_FILES = {k: os.path.join(ROOT, "profiles", f"{k}_dense_llm_traffic.md")
+                 for k in ("fold_step_unfold_kernel", "fold_step_kernel", "step_kernel")}
+KERNEL_OF_PATH = {"fused_unpack": "fold_step_unfold_kernel", "fused": "fold_step_kernel",
+                  "unfused": "step_kernel"}
 KERNEL_SRC = os.path.join(ROOT, "blockwise_fp8_zero_amd", "csrc", "kernels.hip")
 
 
@@ -147,9 +152,8 @@ def main():
     ap.add_argument("--workload", default="dense_llm",
                     choices=["dense_llm", "ragged", "moe_experts", "large", "tiny"])
     ap.add_argument("--skip-cpu-baseline", action="store_true")
-    ap.add_argument("--unfused", action="store_true",
-                    help="time pack_shard + adamw_fp8_step + unpack_fp8 instead of "
-                         "fold_adamw_fp8_step + unpack_fp8")
+    ap.add_argument("--path", default="fused_unpack", choices=list(KERNEL_OF_PATH),
+                    help="which entry points make up a step (see the module docstring)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -166,13 +170,13 @@ def main():
     w = WL.BY_NAME[args.workload]()
     log(f"workload {w.name}: {w.description}")
     t0 = time.perf_counter()
-    g = GpuWorkload(w, fused=not args.unfused)
+    g = GpuWorkload(w, mode=args.path)
     g.load_state()
     prior = w.steps[:-1]
     if prior:
         g.run_steps(prior)
     g.draw_grads(w.measured_step)
-    fp8, sc = g.alloc_rowmajor_out()
+    fp8, sc = g.alloc_rowmajor_out() if args.path != "fused_unpack" else (None, None)
     # a plain 1 GiB device copy, outside the timed region: the reference
     # kernel of known size for scaling the HBM byte counters
     a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -186,17 +190,20 @@ def main():
     t_next = w.measured_step
 
     def one_step(t, ev=None):
-        if args.unfused:
+        if args.path == "unfused":
             g.pack_grads()
         if ev is not None:
             ev[0].record(stream)
-        if args.unfused:
+        if args.path == "unfused":
             g.step(t)
-        else:
+        elif args.path == "fused":
             g.fold_step(t)
+        else:
+            g.fold_step_unpack(t)
         if ev is not None:
             ev[1].record(stream)
-        g.unpack(fp8, sc)
+        if args.path != "fused_unpack":
+            g.unpack(fp8, sc)
 
     for _ in range(args.warmup):
         one_step(t_next)
@@ -220,16 +227,20 @@ def main():
 
     elems = g.q * bfz.TILE_ELEMS
     valid = int((g.table[:g.owned, 4] * g.table[:g.owned, 5]).sum())
-    kernel = "step_kernel" if args.unfused else "fold_step_kernel"
-    # the fused kernel reads the gradient of valid elements only
-    grad_elems = elems if args.unfused else valid
+    kernel = KERNEL_OF_PATH[args.path]
+    # fused kernels read the gradient of valid elements only
+    grad_elems = elems if args.path == "unfused" else valid
     algo_bytes = (STEP_BYTES_PER_ELEM - 4) * elems + 4 * grad_elems + STEP_BYTES_PER_TILE * g.q
+    if args.path == "fused_unpack":
+        # row-major codes of the valid elements and the scale-grid cells
+        algo_bytes += valid + 4 * g.owned
     achieved = algo_bytes / (step_kernel_ms * 1e-3) / 1e9
-    whole_bytes = algo_bytes + UNPACK_BYTES_PER_ELEM * elems + UNPACK_BYTES_PER_TILE * g.q
-    if args.unfused:
+    whole_bytes = algo_bytes
+    if args.path != "fused_unpack":
+        whole_bytes += UNPACK_BYTES_PER_ELEM * elems + UNPACK_BYTES_PER_TILE * g.q
+    if args.path == "unfused":
         whole_bytes += PACK_BYTES_PER_ELEM * elems
     traffic = measured_traffic(kernel) if w.name == "dense_llm" else None
-
     out = {
         "metric": METRIC,
         "value": elems / (ms_per_step * 1e-3),
@@ -251,8 +262,9 @@ def main():
             "D": w.D,
             "rank": w.rank,
             "first_timed_step_t": w.measured_step + args.warmup,
-            "step_path": ("pack_shard(grad) + adamw_fp8_step + unpack_fp8" if args.unfused
-                          else "fold_adamw_fp8_step + unpack_fp8"),
+            "step_path": {"unfused": "pack_shard(grad) + adamw_fp8_step + unpack_fp8",
+                          "fused": "fold_adamw_fp8_step + unpack_fp8",
+                          "fused_unpack": "fold_adamw_fp8_step_unpack"}[args.path],
         },
         "step_hbm_GBps": whole_bytes / (ms_per_step * 1e-3) / 1e9,
         "step_hbm_frac": whole_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,

@@ -59,6 +59,9 @@ int launch_step(float* master, const float* grad, float* m, float* v, uint8_t* c
 int launch_fold_step(const TileEntry* d_entries, int64_t n_slots, const PackArgs& grads,
                      float* master, float* m, float* v, uint8_t* codes, float* scale_inv,
                      const StepScalars& s, void* stream);
+int launch_fold_step_unfold(const TileEntry* d_entries, int64_t n_slots, const PackArgs& grads,
+                            const UnpackArgs& outs, float* master, float* m, float* v,
+                            uint8_t* codes, float* scale_inv, const StepScalars& s, void* stream);
 int launch_encode(const float* in, uint8_t* out, int64_t n, void* stream);
 const char* hip_error_string(int err);
 

@@ -133,12 +133,37 @@ struct RowMajorGrad {
     }
 };
 
+// Where a tile's codes and scale go besides the tile-major shard: straight
+// into the row-major FP8 weight and its scale grid (the unfold done in the
+// same pass).  origin == nullptr: nowhere else.  Thread t's word of 4 codes
+// for float4 k belongs at row 32 k + t / 32, columns 4 (t % 32) .. +3.
+struct RowMajorCodes {
+    uint8_t* origin;      // the tile's element (0, 0) in the FP8 weight
+    float* scale_cell;    // its cell of the scale grid
+    int32_t ld;
+    int16_t rows, cols;
+    bool vec;             // W % 4 == 0 and the weight is 4-byte aligned
+    __device__ __forceinline__ void put(int k, uint32_t word) const {
+        const int r = k * 32 + (threadIdx.x >> 5), c = 4 * (threadIdx.x & 31);
+        if (origin == nullptr || r >= rows) return;
+        uint8_t* q = origin + (int64_t)r * ld + c;
+        if (vec && c + 4 <= cols) {
+            store_stream(reinterpret_cast<uint32_t*>(q), word);
+            return;
+        }
+#pragma unroll
+        for (int l = 0; l < 4; ++l)
+            if (c + l < cols) q[l] = (uint8_t)(word >> (8 * l));
+    }
+};
+
 template <class GradFn>
 __device__ __forceinline__ void step_tile(int64_t tile, float* __restrict__ master,
                                           float* __restrict__ mom1, float* __restrict__ mom2,
                                           uint32_t* __restrict__ codes,
                                           float* __restrict__ scale_inv, const StepScalars& s,
-                                          const GradFn& grad_at, float* wave_amax) {
+                                          const GradFn& grad_at, float* wave_amax,
+                                          const RowMajorCodes& out = RowMajorCodes{}) {
     const int64_t base = tile * (kTileElems / 4);
     f32x4* P = reinterpret_cast<f32x4*>(master) + base;
     f32x4* M = reinterpret_cast<f32x4*>(mom1) + base;
@@ -181,11 +206,17 @@ __device__ __forceinline__ void step_tile(int64_t tile, float* __restrict__ mast
     // scale_inv = amax / 448; an all-zero tile takes 1 and codes 0.
     const bool zero = amax == 0.0f;
     const float scale = zero ? 1.0f : amax / 448.0f;
-    if (threadIdx.x == 0) scale_inv[tile] = scale;
-    uint32_t* C = codes + base;
+    if (threadIdx.x == 0) {
+        if (scale_inv) scale_inv[tile] = scale;
+        if (out.scale_cell) *out.scale_cell = scale;
+    }
+    uint32_t* C = codes ? codes + base : nullptr;
 #pragma unroll
-    for (int k = 0; k < kStepVec; ++k)
-        store_stream(C + k * kStepThreads + threadIdx.x, zero ? 0u : pack_codes(p[k], scale));
+    for (int k = 0; k < kStepVec; ++k) {
+        const uint32_t word = zero ? 0u : pack_codes(p[k], scale);
+        if (C) store_stream(C + k * kStepThreads + threadIdx.x, word);
+        out.put(k, word);
+    }
 }
 
 __global__ __launch_bounds__(kStepThreads) void step_kernel(
@@ -215,6 +246,30 @@ __global__ __launch_bounds__(kStepThreads) void fold_step_kernel(
         g.vec = ((t.ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(w) & 15u) == 0);
     }
     step_tile(slot, master, mom1, mom2, codes, scale_inv, s, g, wave_amax);
+}
+
+// Fold, step and unfold in one pass: as fold_step_kernel, and each owned
+// tile's codes and scale also land in the row-major FP8 weight and scale
+// grid its entry names.  codes / scale_inv may be null (row-major only).
+__global__ __launch_bounds__(kStepThreads) void fold_step_unfold_kernel(
+    const TileEntry* __restrict__ entries, PackArgs grads, UnpackArgs outs,
+    float* __restrict__ master, float* __restrict__ mom1, float* __restrict__ mom2,
+    uint32_t* __restrict__ codes, float* __restrict__ scale_inv, StepScalars s, int64_t n_slots) {
+    extern __shared__ float wave_amax[];
+    const int64_t slot = xcd_tile(blockIdx.x, n_slots);
+    const TileEntry t = entries[slot];
+    RowMajorGrad g{nullptr, t.ld, t.valid_rows, t.valid_cols, false};
+    RowMajorCodes out{nullptr, nullptr, t.ld, t.valid_rows, t.valid_cols, false};
+    if (t.local >= 0) {
+        const float* w = grads.src[t.local];
+        g.origin = w + t.base;
+        g.vec = ((t.ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(w) & 15u) == 0);
+        uint8_t* d = outs.codes[t.local];
+        out.origin = d + t.base;
+        out.scale_cell = outs.scale[t.local] + t.scale_index;
+        out.vec = ((t.ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(d) & 3u) == 0);
+    }
+    step_tile(slot, master, mom1, mom2, codes, scale_inv, s, g, wave_amax, out);
 }
 
 // Fold: one workgroup per slot.  Thread t copies float4 column t % 32 of
@@ -332,7 +387,7 @@ hipError_t reserve_lds(const void* kernel, std::atomic<uint64_t>& ready) {
     return hipSuccess;
 }
 
-std::atomic<uint64_t> g_step_lds{0}, g_fold_step_lds{0};
+std::atomic<uint64_t> g_step_lds{0}, g_fold_step_lds{0}, g_fold_step_unfold_lds{0};
 
 }  // namespace
 
@@ -355,6 +410,19 @@ int launch_fold_step(const TileEntry* d_entries, int64_t n_slots, const PackArgs
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(fold_step_kernel, dim3((uint32_t)n_slots), dim3(kStepThreads),
                        kStepLdsBytes, (hipStream_t)stream, d_entries, grads, master, m, v,
+                       reinterpret_cast<uint32_t*>(codes), scale_inv, s, n_slots);
+    return hipGetLastError();
+}
+
+int launch_fold_step_unfold(const TileEntry* d_entries, int64_t n_slots, const PackArgs& grads,
+                            const UnpackArgs& outs, float* master, float* m, float* v,
+                            uint8_t* codes, float* scale_inv, const StepScalars& s, void* stream) {
+    if (n_slots == 0) return hipSuccess;
+    hipError_t err = reserve_lds(reinterpret_cast<const void*>(fold_step_unfold_kernel),
+                                 g_fold_step_unfold_lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(fold_step_unfold_kernel, dim3((uint32_t)n_slots), dim3(kStepThreads),
+                       kStepLdsBytes, (hipStream_t)stream, d_entries, grads, outs, master, m, v,
                        reinterpret_cast<uint32_t*>(codes), scale_inv, s, n_slots);
     return hipGetLastError();
 }

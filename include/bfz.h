@@ -16,7 +16,8 @@
  *      row-major scale grid (unpack_fp8; the unfold of "Parameter layout
  *      transform" and "Summary").
  * fold_adamw_fp8_step does 1 and 2 in one pass, reading the gradients
- * straight from their row-major weights.
+ * straight from their row-major weights; fold_adamw_fp8_step_unpack does
+ * 1, 2 and 3 in one pass.
  *
  * Conventions shared by every call:
  *   - A tile is 16384 contiguous elements: 128 rows of 128, row-major.
@@ -24,9 +25,10 @@
  *   - Device pointers are caller-owned (the library never frees them); the
  *     library allocates only the plan's small device table, in
  *     bfz_plan_upload, freed by bfz_plan_destroy.
- *   - pack_shard, adamw_fp8_step, fold_adamw_fp8_step and unpack_fp8 are
- *     asynchronous on the HIP stream passed as `stream` (NULL = the null
- *     stream): they only enqueue kernels, never allocate, never synchronize.
+ *   - pack_shard, adamw_fp8_step, fold_adamw_fp8_step,
+ *     fold_adamw_fp8_step_unpack and unpack_fp8 are asynchronous on the HIP
+ *     stream passed as `stream` (NULL = the null stream): they only enqueue
+ *     kernels, never allocate, never synchronize.
  *   - Return value: 0 on success, else a negative BFZ_E* code; the message
  *     for the calling thread's last failure is bfz_last_error().
  *   - Non-finite inputs (NaN, Inf) give unspecified results.
@@ -162,6 +164,28 @@ int adamw_fp8_step(float* master, const float* grad, float* m, float* v, uint8_t
 int fold_adamw_fp8_step(const bfz_plan* plan, const float* const* grad, float* master, float* m,
                         float* v, uint8_t* codes, float* scale_inv, const bfz_adamw* hp,
                         void* stream);
+
+/*
+ * fold_adamw_fp8_step and unpack_fp8 in one pass: the same results, bit for
+ * bit, as
+ *     fold_adamw_fp8_step(plan, grad, master, m, v, codes, scale_inv, hp, stream);
+ *     unpack_fp8(plan, codes, scale_inv, dst_fp8, dst_scale, stream);
+ * with each tile's codes and scale written straight into the row-major FP8
+ * weight and scale grid from the registers that produced them (the unfold
+ * of "Parameter layout transform" / "Summary" done inside the update; the
+ * rank's own tiles need no second pass).  codes and scale_inv may both be
+ * NULL when no tile-major copy is wanted (e.g. a single rank, D = 1, with
+ * nothing to all-gather); otherwise both are written as in adamw_fp8_step.
+ * dst_fp8 / dst_scale: as in unpack_fp8 (entries of weights the rank does
+ * not touch may be NULL; 4-byte aligned rows whose W is a multiple of 4
+ * take 32-bit stores).  Other arguments as in fold_adamw_fp8_step.
+ * Errors: BFZ_EINVAL (incl. exactly one of codes / scale_inv NULL),
+ *         BFZ_EALIGN, BFZ_ESTATE, BFZ_EHIP.
+ */
+int fold_adamw_fp8_step_unpack(const bfz_plan* plan, const float* const* grad, float* master,
+                               float* m, float* v, uint8_t* codes, float* scale_inv,
+                               uint8_t* const* dst_fp8, float* const* dst_scale,
+                               const bfz_adamw* hp, void* stream);
 
 /*
  * Unfold of the rank's owned slots: dst_fp8[p][e][128 i + a][128 j + b] =

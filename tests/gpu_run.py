@@ -21,11 +21,17 @@ def hp_for(w, t):
 class GpuWorkload:
     """Device state of one rank's shard of workload w."""
 
-    def __init__(self, w: WL.Workload, device="cuda", fused=False):
-        """fused: take each step with fold_adamw_fp8_step (gradients read
-        row-major) instead of pack_shard + adamw_fp8_step."""
+    MODES = ("unfused", "fused", "fused_unpack")
+
+    def __init__(self, w: WL.Workload, device="cuda", mode="unfused"):
+        """mode: how a step is taken --
+        "unfused": pack_shard + adamw_fp8_step (then unpack_fp8 on demand);
+        "fused": fold_adamw_fp8_step (gradients read row-major);
+        "fused_unpack": fold_adamw_fp8_step_unpack, which also writes the
+        row-major FP8 weights and scale grids (self.out_fp8 / self.out_scale)."""
+        assert mode in self.MODES, mode
         self.w = w
-        self.fused = fused
+        self.mode = mode
         self.device = torch.device(device)
         with torch.cuda.device(self.device):
             self.plan = bfz.Plan(w.dims, w.D, w.rank)
@@ -45,6 +51,9 @@ class GpuWorkload:
         self.scale_inv = torch.empty(self.q, dtype=torch.float32, **kw)
         self.grad_rm = None
         self.t_done = 0
+        self.out_fp8 = self.out_scale = None
+        if mode == "fused_unpack":
+            self.out_fp8, self.out_scale = self.alloc_rowmajor_out()
 
     # ---- inputs ------------------------------------------------------------
     def _rowmajor(self, tensor, step=0):
@@ -81,13 +90,29 @@ class GpuWorkload:
         bfz.fold_adamw_fp8_step(self.plan, self.grad_rm, self.master, self.m, self.v, self.codes,
                                 self.scale_inv, hp_for(self.w, t))
 
+    def fold_step_unpack(self, t):
+        bfz.fold_adamw_fp8_step_unpack(self.plan, self.grad_rm, self.master, self.m, self.v,
+                                       self.codes, self.scale_inv, self.out_fp8, self.out_scale,
+                                       hp_for(self.w, t))
+
     def apply(self, t):
         """One step on the current row-major gradients."""
-        if self.fused:
+        if self.mode == "fused":
             self.fold_step(t)
+        elif self.mode == "fused_unpack":
+            self.fold_step_unpack(t)
         else:
             self.pack_grads()
             self.step(t)
+
+    def rowmajor(self):
+        """Row-major FP8 weights and scale grids of the owned tiles: those the
+        last step wrote (fused_unpack), else a fresh unpack_fp8."""
+        if self.mode == "fused_unpack":
+            return self.out_fp8, self.out_scale
+        fp8, sc = self.alloc_rowmajor_out()
+        self.unpack(fp8, sc)
+        return fp8, sc
 
     def run_steps(self, steps=None):
         """Draw, fold and apply the grads of each step counter in `steps`."""

@@ -41,14 +41,14 @@ def _check(gpu, ora, what):
     return rep
 
 
-MODES = ["pack+step", "fused"]
+MODES = list(GpuWorkload.MODES)
 
 
 @pytest.mark.parametrize("mode", MODES)
 def test_tiny_every_step_every_slot(mode):
     w = WL.tiny()
     _say("tiny: 256x384, 3 steps, seed", w.seed, "mode", mode)
-    g = GpuWorkload(w, fused=mode == "fused")
+    g = GpuWorkload(w, mode=mode)
     g.load_state()
     slots = list(range(g.q))
     for k, t in enumerate(w.steps):
@@ -57,8 +57,7 @@ def test_tiny_every_step_every_slot(mode):
         rep = _check(g.tiles(slots), ora, f"tiny after t={t}")
         assert rep["exact"], "the step is expected to be bit-exact with the oracle"
     # unfold of the final codes and scales
-    fp8, sc = g.alloc_rowmajor_out()
-    g.unpack(fp8, sc)
+    fp8, sc = g.rowmajor()
     q, owned, table = oracle.plan(w.dims, w.D, w.rank)
     E, H, W = w.dims[0]
     o8 = np.zeros((E, H, W), dtype=np.uint8)
@@ -72,7 +71,7 @@ def test_tiny_every_step_every_slot(mode):
 def test_ragged_every_slot(mode):
     w = WL.ragged()
     _say("ragged: 40 matrices, D=8 rank 3, seed", w.seed, "mode", mode)
-    g = GpuWorkload(w, fused=mode == "fused")
+    g = GpuWorkload(w, mode=mode)
     g.load_state()
     g.run_steps()
     slots = list(range(g.q))
@@ -80,8 +79,7 @@ def test_ragged_every_slot(mode):
     rep = _check(g.tiles(slots), ora, "ragged")
     assert rep["exact"]
     # unfold into the ragged row-major weights
-    fp8, sc = g.alloc_rowmajor_out()
-    g.unpack(fp8, sc)
+    fp8, sc = g.rowmajor()
     q, owned, table = oracle.plan(w.dims, w.D, w.rank)
     o8 = [None] * len(w.dims)
     osc = [None] * len(w.dims)
@@ -103,7 +101,7 @@ def test_full_size_sampled(name, mode):
     w = WL.BY_NAME[name]()
     _say(name, "full size,", len(w.dims), "weights, D =", w.D, "rank", w.rank, "seed", w.seed,
          "mode", mode)
-    g = GpuWorkload(w, fused=mode == "fused")
+    g = GpuWorkload(w, mode=mode)
     g.load_state()
     g.run_steps()
     slots = sample_slots(w)
@@ -117,8 +115,7 @@ def test_full_size_sampled(name, mode):
         assert zero, "sample holds no all-zero tile"
         assert (ora["scale_inv"][zero] == 1.0).all()
         # row-major FP8 + scale grid, checked at the sampled tiles
-        fp8, sc = g.alloc_rowmajor_out()
-        g.unpack(fp8, sc)
+        fp8, sc = g.rowmajor()
         torch.cuda.synchronize()
         for k, s in enumerate(slots):
             p, e, i, j, vr, vc = (int(x) for x in ora["table"][k])
@@ -142,7 +139,7 @@ def test_rank_decomposition_is_invariant(mode):
     w1.dims = w1.dims[:6]
     w1.D, w1.rank = 1, 0
     _say("rank invariance: 6 ragged matrices, D in {1, 3, 7}, mode", mode)
-    ref = GpuWorkload(w1, fused=mode == "fused")
+    ref = GpuWorkload(w1, mode=mode)
     ref.load_state()
     ref.run_steps()
     full = ref.tiles(list(range(ref.owned)))
@@ -151,7 +148,7 @@ def test_rank_decomposition_is_invariant(mode):
         for r in range(D):
             w = WL.ragged()
             w.dims, w.D, w.rank = w1.dims, D, r
-            g = GpuWorkload(w, fused=mode == "fused")
+            g = GpuWorkload(w, mode=mode)
             g.load_state()
             g.run_steps()
             if g.owned:
@@ -215,9 +212,10 @@ def test_deterministic_and_empty():
     assert torch.equal(before, g.codes)
 
 
-def test_fused_equals_unfused_on_misaligned_gradients():
+def test_fused_routes_equal_unfused_on_misaligned_buffers():
     """Gradients that start 4 bytes into their buffer (no 16-byte vector
-    path) give the same bits through both routes."""
+    path) and FP8 destinations that start 1 byte in (no 32-bit stores) give
+    the same bits through all three routes, and without the tile-major copy."""
     dims = [(1, 300, 260), (2, 129, 516), (1, 128, 128)]
     _say("fused vs pack+step, misaligned gradients, seed 21")
     rng = np.random.default_rng(21)
@@ -233,22 +231,36 @@ def test_fused_equals_unfused_on_misaligned_gradients():
     for d in dims:
         raw = torch.from_numpy(rng.normal(0, 1e-3, int(np.prod(d)) + 1).astype(np.float32)).cuda()
         grads.append(raw[1:])
+    hb = [(d[0], -(-d[1] // 128), -(-d[2] // 128)) for d in dims]
     outs = []
-    for fused in (False, True):
+    for route in ("unfused", "fused", "fused_unpack", "rowmajor_only"):
         p, m, v = (x.clone() for x in state0)
-        codes = torch.empty(n, dtype=torch.uint8, device="cuda")
-        sc = torch.empty(q, dtype=torch.float32, device="cuda")
+        codes = torch.zeros(n, dtype=torch.uint8, device="cuda")
+        sc = torch.zeros(q, dtype=torch.float32, device="cuda")
+        raw8 = [torch.zeros(int(np.prod(d)) + 1, dtype=torch.uint8, device="cuda") for d in dims]
+        d8 = [r[1:] for r in raw8]
+        dsc = [torch.zeros(int(np.prod(h)), dtype=torch.float32, device="cuda") for h in hb]
         hp = bfz.AdamW(step=5, **WL.HP)
-        if fused:
-            bfz.fold_adamw_fp8_step(plan, grads, p, m, v, codes, sc, hp)
-        else:
+        if route == "unfused":
             gt = torch.empty(n, dtype=torch.float32, device="cuda")
             bfz.pack_shard(plan, grads, gt)
             bfz.adamw_fp8_step(p, gt, m, v, codes, sc, hp)
+            bfz.unpack_fp8(plan, codes, sc, d8, dsc)
+        elif route == "fused":
+            bfz.fold_adamw_fp8_step(plan, grads, p, m, v, codes, sc, hp)
+            bfz.unpack_fp8(plan, codes, sc, d8, dsc)
+        elif route == "fused_unpack":
+            bfz.fold_adamw_fp8_step_unpack(plan, grads, p, m, v, codes, sc, d8, dsc, hp)
+        else:
+            bfz.fold_adamw_fp8_step_unpack(plan, grads, p, m, v, None, None, d8, dsc, hp)
         torch.cuda.synchronize()
-        outs.append([x.cpu().numpy() for x in (p, m, v, codes, sc)])
-    for a, b in zip(*outs):
-        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+        outs.append([x.cpu().numpy() for x in [p, m, v, codes, sc] + d8 + dsc])
+    for r in range(1, 4):
+        for k, (a, b) in enumerate(zip(outs[0], outs[r])):
+            if r == 3 and k in (3, 4):
+                assert not b.any()  # no tile-major copy requested
+                continue
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), (r, k)
 
 
 def test_misaligned_pointer_is_rejected():
