@@ -17,7 +17,7 @@
 namespace bfz {
 namespace {
 
-constexpr int kThreads = 256;  // fold / unfold / encode: 4 wave64s per workgroup
+constexpr int kThreads = 256;  // unfold / encode: 4 wave64s per workgroup
 
 // ---------------------------------------------------------------------
 // E4M3 (OCP E4M3FN) rounding of a binary32 value: nearest value, ties to
@@ -272,51 +272,27 @@ __global__ __launch_bounds__(kStepThreads) void fold_step_unfold_kernel(
     step_tile(slot, master, mom1, mom2, codes, scale_inv, s, g, wave_amax, out);
 }
 
-// Fold: one workgroup per slot.  Thread t copies float4 column t % 32 of
-// rows t / 32, t / 32 + 8, ...: a wave covers two whole 512-byte tile rows
-// per load, so both the strided row-major reads and the contiguous tile
-// writes are coalesced.  Outside the weight's edge, and in padding slots,
-// the tile gets +0.0.
-__global__ __launch_bounds__(kThreads) void pack_kernel(const TileEntry* __restrict__ entries,
-                                                        float* __restrict__ dst, PackArgs args) {
-    const int64_t slot = blockIdx.x;
+// Fold: one 1024-thread workgroup per slot, the step kernels' thread
+// layout: thread t moves float4 column t % 32 of rows t / 32 + 32 k, k < 4,
+// so a wave covers two 512-byte tile rows per instruction on both sides.
+// All four loads are issued before the stores; streaming accesses.  Outside
+// the weight's edge, and in padding slots, the tile gets +0.0.
+__global__ __launch_bounds__(kStepThreads) void pack_kernel(const TileEntry* __restrict__ entries,
+                                                            float* __restrict__ dst, PackArgs args) {
+    const int64_t slot = xcd_tile(blockIdx.x, gridDim.x);
     const TileEntry t = entries[slot];
-    float4* out = reinterpret_cast<float4*>(dst + slot * kTileElems);
-    const int c4 = threadIdx.x & 31;
-    const int r0 = threadIdx.x >> 5;
-    if (t.local < 0) {
+    f32x4* out = reinterpret_cast<f32x4*>(dst + slot * kTileElems);
+    RowMajorGrad src{nullptr, t.ld, t.valid_rows, t.valid_cols, false};
+    if (t.local >= 0) {
+        const float* w = args.src[t.local];
+        src.origin = w + t.base;
+        src.vec = ((t.ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(w) & 15u) == 0);
+    }
+    f32x4 x[kStepVec];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) out[(r0 + 8 * k) * 32 + c4] = make_float4(0.f, 0.f, 0.f, 0.f);
-        return;
-    }
-    const float* src = args.src[t.local] + t.base;
-    const bool vec = ((t.ld & 3) == 0) &&
-                     ((reinterpret_cast<uintptr_t>(args.src[t.local]) & 15u) == 0);
-    const int col = 4 * c4;
-    if (vec && t.valid_rows == kTileDim && t.valid_cols == kTileDim) {
+    for (int k = 0; k < kStepVec; ++k) x[k] = src(k);
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int r = r0 + 8 * k;
-            out[r * 32 + c4] = *reinterpret_cast<const float4*>(src + (int64_t)r * t.ld + col);
-        }
-        return;
-    }
-    for (int k = 0; k < 16; ++k) {
-        const int r = r0 + 8 * k;
-        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (r < t.valid_rows) {
-            const float* row = src + (int64_t)r * t.ld + col;
-            if (vec && col + 4 <= t.valid_cols) {
-                x = *reinterpret_cast<const float4*>(row);
-            } else {
-                if (col + 0 < t.valid_cols) x.x = row[0];
-                if (col + 1 < t.valid_cols) x.y = row[1];
-                if (col + 2 < t.valid_cols) x.z = row[2];
-                if (col + 3 < t.valid_cols) x.w = row[3];
-            }
-        }
-        out[r * 32 + c4] = x;
-    }
+    for (int k = 0; k < kStepVec; ++k) store_stream(out + k * kStepThreads + threadIdx.x, x[k]);
 }
 
 // Unfold of codes and scales: one workgroup per owned slot.  Thread t moves
@@ -344,7 +320,9 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const TileEntry* __res
         const uint4 x = in[r * 8 + c16];
         uint8_t* row = dst + (int64_t)r * t.ld + col;
         if (col + 16 <= t.valid_cols && vec16) {
-            *reinterpret_cast<uint4*>(row) = x;
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 y = {x.x, x.y, x.z, x.w};
+            __builtin_nontemporal_store(y, reinterpret_cast<u32x4*>(row));
         } else if (col + 16 <= t.valid_cols && vec4) {
             uint32_t* r4 = reinterpret_cast<uint32_t*>(row);
             r4[0] = x.x;
@@ -430,7 +408,7 @@ int launch_fold_step_unfold(const TileEntry* d_entries, int64_t n_slots, const P
 int launch_pack(const TileEntry* d_entries, int64_t n_slots, float* dst, const PackArgs& args,
                 void* stream) {
     if (n_slots == 0) return hipSuccess;
-    hipLaunchKernelGGL(pack_kernel, dim3((uint32_t)n_slots), dim3(kThreads), 0,
+    hipLaunchKernelGGL(pack_kernel, dim3((uint32_t)n_slots), dim3(kStepThreads), 0,
                        (hipStream_t)stream, d_entries, dst, args);
     return hipGetLastError();
 }

@@ -163,6 +163,40 @@ def test_rank_decomposition_is_invariant(mode):
             assert np.array_equal(cat.view(np.uint8), full[k].view(np.uint8)), (D, k)
 
 
+def test_full_model_unfold_after_allgather():
+    """Every rank steps its shard; the all-gather of the tile-major codes and
+    scales is their concatenation in rank order, which puts every global tile
+    at its global index -- so unpack_fp8 with the single-rank plan unfolds
+    the whole model.  It must equal the single-rank run's row-major output."""
+    dims = WL.ragged().dims[:7]
+    D = 4
+    _say("full-model unfold after all-gather: 7 ragged matrices, D =", D)
+    codes, scales = [], []
+    for r in range(D):
+        w = WL.ragged()
+        w.dims, w.D, w.rank = dims, D, r
+        g = GpuWorkload(w, mode="fused_unpack")
+        g.load_state()
+        g.run_steps()
+        codes.append(g.codes)
+        scales.append(g.scale_inv)
+    w1 = WL.ragged()
+    w1.dims, w1.D, w1.rank = dims, 1, 0
+    ref = GpuWorkload(w1, mode="fused_unpack")
+    ref.load_state()
+    ref.run_steps()
+    T = ref.q
+    gathered_codes = torch.cat(codes)[:T * 16384].contiguous()
+    gathered_scales = torch.cat(scales)[:T].contiguous()
+    fp8, sc = ref.alloc_rowmajor_out()
+    bfz.unpack_fp8(ref.plan, gathered_codes, gathered_scales, fp8, sc)
+    torch.cuda.synchronize()
+    want8, wantsc = ref.rowmajor()
+    for p in ref.touched:
+        assert torch.equal(fp8[p], want8[p]), p
+        assert torch.equal(sc[p], wantsc[p]), p
+
+
 def test_amax_at_every_position():
     """16384 tiles; tile k has its largest |value| at element k (sign
     alternating).  lr = 0 leaves the master unchanged, so the scale must be
