@@ -51,6 +51,7 @@ def lib():
             getattr(L, n).restype = i64
         L.bfz_plan_table.argtypes = [P, P]
         L.bfz_plan_tile.argtypes = [P, i64, P]
+        L.bfz_paramwise_split.argtypes = [P, i32, i32, P, P]
         L.pack_shard.argtypes = [P, P, P, P]
         L.adamw_fp8_step.argtypes = [P, P, P, P, P, P, i64, C.POINTER(AdamW), P]
         L.fold_adamw_fp8_step.argtypes = [P, P, P, P, P, P, P, C.POINTER(AdamW), P]
@@ -143,6 +144,18 @@ class Plan:
             self.close()
         except Exception:
             pass
+
+
+def paramwise_split(dims, D):
+    """The page's param-wise split, for comparison: (bucket_of_param int32 [n],
+    bucket_elems int64 [D])."""
+    import numpy as np
+    flat = (C.c_int64 * (3 * max(1, len(dims))))(*[int(x) for d in dims for x in d])
+    bop = np.empty(len(dims), dtype=np.int32)
+    be = np.empty(D, dtype=np.int64)
+    _check(lib().bfz_paramwise_split(C.cast(flat, C.c_void_p), len(dims), D,
+                                     bop.ctypes.data_as(C.c_void_p), be.ctypes.data_as(C.c_void_p)))
+    return bop, be
 
 
 def _ptr_array(tensors, dtype, name, n):

@@ -113,6 +113,37 @@ extern "C" int bfz_plan_create(const int64_t* dims, int32_t n_weights, int32_t D
     return BFZ_OK;
 }
 
+// "Param-wise split" (the alternative the page rejects, kept to compare
+// padding): weights sorted by size, largest first, each dealt to the bucket
+// with the fewest elements so far; every bucket is then padded to the
+// largest.  Ties: equal sizes keep their declared order, equal buckets go to
+// the lower index.
+extern "C" int bfz_paramwise_split(const int64_t* dims, int32_t n_weights, int32_t D,
+                                   int32_t* bucket_of_weight, int64_t* bucket_elems) {
+    using namespace bfz;
+    if (!dims || !bucket_of_weight || !bucket_elems)
+        return fail(BFZ_EINVAL, "bfz_paramwise_split: null pointer");
+    if (n_weights < 1 || D < 1)
+        return fail(BFZ_EINVAL, "bfz_paramwise_split: need n_params >= 1 and D >= 1");
+    std::vector<std::pair<int64_t, int32_t>> order(n_weights);
+    for (int32_t p = 0; p < n_weights; ++p) {
+        const int64_t E = dims[3 * p], H = dims[3 * p + 1], W = dims[3 * p + 2];
+        if (E < 1 || H < 1 || W < 1 || H > (int64_t(1) << 31) || W > (int64_t(1) << 31) ||
+            E > (int64_t(1) << 62) / (H * W))
+            return fail(BFZ_EINVAL, "bfz_paramwise_split: weight %d has bad dims", p);
+        order[p] = {E * H * W, p};
+    }
+    std::stable_sort(order.begin(), order.end(),
+                     [](const auto& a, const auto& b) { return a.first > b.first; });
+    std::fill(bucket_elems, bucket_elems + D, int64_t(0));
+    for (const auto& [size, p] : order) {
+        const int32_t b = int32_t(std::min_element(bucket_elems, bucket_elems + D) - bucket_elems);
+        bucket_of_weight[p] = b;
+        bucket_elems[b] += size;
+    }
+    return BFZ_OK;
+}
+
 extern "C" void bfz_plan_destroy(bfz_plan* plan) {
     if (!plan) return;
     if (plan->d_entries) {

@@ -105,6 +105,21 @@ int bfz_plan_table(const bfz_plan* plan, int64_t* out);
 int bfz_plan_tile(const bfz_plan* plan, int64_t slot, int64_t out[6]);
 
 /*
+ * The param-wise split of "A ZeRO Optimizer Design for Blockwise FP8
+ * Quantization", section "Param-wise split" -- the alternative the page
+ * replaces with the block-wise split, provided to compare their padding:
+ * each weight stays whole on one rank; weights are taken largest first
+ * (E H W elements; equal sizes in declared order) and each goes to the
+ * bucket holding the fewest elements so far (the lower index on ties);
+ * every bucket is then padded to the largest.  Host only.
+ * dims as in bfz_plan_create.  Out: bucket_of_param[n_params] in [0, D),
+ * bucket_elems[D] the elements per bucket (padded shard = their maximum).
+ * Errors: BFZ_EINVAL.
+ */
+int bfz_paramwise_split(const int64_t* dims, int32_t n_params, int32_t D,
+                        int32_t* bucket_of_param, int64_t* bucket_elems);
+
+/*
  * Fold: dst[s][a][b] = src[p][e][128 i + a][128 j + b] for the weight p,
  * expert e and tile (i, j) of slot s, and +0.0 outside the weight's edge
  * and in padding slots.

@@ -45,6 +45,8 @@ def lib():
         L.ora_total_tiles.restype = C.c_int64
         L.ora_plan.argtypes = [P, C.c_int32, C.c_int32, C.c_int32, P, P, P]
         L.ora_plan.restype = C.c_int
+        L.ora_paramwise_split.argtypes = [P, C.c_int32, C.c_int32, P, P]
+        L.ora_paramwise_split.restype = C.c_int
         L.ora_fold_tile.argtypes = [P, C.c_int64, C.c_int64, C.c_int64, C.c_int64, C.c_int64, P]
         L.ora_pack.argtypes = [P, C.c_int32, P, P, C.c_int64, P]
         L.ora_unpack.argtypes = [P, C.c_int32, P, P, P, C.c_int64, P, P]
@@ -107,6 +109,16 @@ def plan(dims, D: int, rank: int):
     table = np.empty((q.value, 6), dtype=np.int64)
     lib().ora_plan(_ptr(d), d.shape[0], D, rank, C.byref(q), C.byref(owned), _ptr(table))
     return q.value, owned.value, table
+
+
+def paramwise_split(dims, D: int):
+    """Returns (bucket_of_param int32 [n], bucket_elems int64 [D])."""
+    d = _dims_array(dims)
+    bop = np.empty(d.shape[0], dtype=np.int32)
+    be = np.empty(D, dtype=np.int64)
+    if lib().ora_paramwise_split(_ptr(d), d.shape[0], D, _ptr(bop), _ptr(be)) != 0:
+        raise ValueError("oracle paramwise_split: invalid arguments")
+    return bop, be
 
 
 # ---- fold / unfold --------------------------------------------------------

@@ -154,6 +154,45 @@ int ora_plan(const int64_t* dims, int32_t n_params, int32_t D, int32_t rank,
     return 0;
 }
 
+/*
+ * [ZeRO-FP8, "Param-wise split"]: the weights are sorted by size and dealt
+ * greedily so that the D buckets come out as even as possible; every bucket
+ * is then padded to the largest one.  Reading of "greedy": largest weight
+ * first, each into the bucket holding the fewest elements so far (ties: the
+ * lower bucket; equal sizes: declared order) -- the longest-processing-time
+ * rule.  A weight is its whole E x H x W tensor; no 128-padding is needed,
+ * since each weight stays whole on one rank.
+ * Parity: the tie-breaking is a reading (parity unpinned); the rule is
+ * pinned by brute-force optima against Graham's LPT bound in
+ * tests/test_oracle_plan.py.
+ */
+int ora_paramwise_split(const int64_t* dims, int32_t n_params, int32_t D,
+                        int32_t* bucket_of_param, int64_t* bucket_elems) {
+    if (n_params < 0 || D < 1) return -1;
+    for (int32_t b = 0; b < D; ++b) bucket_elems[b] = 0;
+    for (int32_t p = 0; p < n_params; ++p) {
+        if (dims[3 * p] < 1 || dims[3 * p + 1] < 1 || dims[3 * p + 2] < 1) return -1;
+        bucket_of_param[p] = -1;
+    }
+    for (int32_t done = 0; done < n_params; ++done) {
+        /* the largest weight not yet placed (first in declared order on ties) */
+        int32_t pick = -1;
+        int64_t pick_size = -1;
+        for (int32_t p = 0; p < n_params; ++p) {
+            if (bucket_of_param[p] >= 0) continue;
+            int64_t size = dims[3 * p] * dims[3 * p + 1] * dims[3 * p + 2];
+            if (size > pick_size) { pick = p; pick_size = size; }
+        }
+        /* the emptiest bucket (lowest index on ties) */
+        int32_t best = 0;
+        for (int32_t b = 1; b < D; ++b)
+            if (bucket_elems[b] < bucket_elems[best]) best = b;
+        bucket_of_param[pick] = best;
+        bucket_elems[best] += pick_size;
+    }
+    return 0;
+}
+
 /* ===================================================================== *
  * Fold / unfold                                                          *
  * ===================================================================== */

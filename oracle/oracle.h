@@ -65,6 +65,12 @@ int64_t ora_total_tiles(const int64_t* dims, int32_t n_params);
 int ora_plan(const int64_t* dims, int32_t n_params, int32_t D, int32_t rank,
              int64_t* q, int64_t* owned, int64_t* table);
 
+/* The param-wise split (compared against, not used by, the block-wise
+ * split): bucket_of_param[p] in [0, D) for each weight, bucket_elems[D] the
+ * elements per bucket.  Returns 0, or -1 on bad input. */
+int ora_paramwise_split(const int64_t* dims, int32_t n_params, int32_t D,
+                        int32_t* bucket_of_param, int64_t* bucket_elems);
+
 /* ---- Fold / unfold ------------------------------------------------ */
 /* One tile of a row-major [E,H,W] fp32 tensor into 128x128 row-major tile
  * storage, zero beyond the tensor's edge. */

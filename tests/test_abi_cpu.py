@@ -56,6 +56,23 @@ def test_plan_of_the_workloads():
         assert np.array_equal(p.table(), table), w.name
 
 
+def test_paramwise_split_matches_oracle():
+    from synth import workloads as WL
+    rng = np.random.default_rng(3)
+    cases = [([(int(rng.integers(1, 3)), int(rng.integers(1, 3000)), int(rng.integers(1, 3000)))
+               for _ in range(int(rng.integers(1, 40)))], int(rng.integers(1, 17))) for _ in range(60)]
+    cases += [([(1, 5, 5)] * 7, 3), ([(2, 4, 4), (1, 8, 4), (1, 4, 8)], 2)]  # size ties
+    cases += [(f().dims, f().D) for f in WL.ALL]
+    for dims, D in cases:
+        a = bfz.paramwise_split(dims, D)
+        b = oracle.paramwise_split(dims, D)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    with pytest.raises(bfz.BfzError):
+        bfz.paramwise_split([(1, 0, 3)], 2)
+    with pytest.raises(bfz.BfzError):
+        bfz.paramwise_split([(1, 2, 3)], 0)
+
+
 @pytest.mark.parametrize("dims,D,rank", [
     ([(1, 10, 10)], 0, 0), ([(1, 10, 10)], 2, 2), ([(1, 10, 10)], 2, -1),
     ([(0, 10, 10)], 1, 0), ([(1, 10, -3)], 1, 0), ([(1, 2 ** 31, 5)], 1, 0), ([], 1, 0),

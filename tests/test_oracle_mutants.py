@@ -42,6 +42,10 @@ MUTANTS = {
     "zero tile scale 0": ("scale_inv[t] = 1.0f;", "scale_inv[t] = 0.0f;"),
     "amax ignores negatives": ("if (fabsf(x[k]) > amax) amax = fabsf(x[k]);", "if (x[k] > amax) amax = x[k];"),
     "quota rounds down": ("int64_t q = ceil_div(T, D);", "int64_t q = T / D + (T % D != 0 && T < D);"),
+    "param-wise: smallest weight first": ("if (size > pick_size) { pick = p; pick_size = size; }",
+                                          "if (pick < 0 || size < pick_size) { pick = p; pick_size = size; }"),
+    "param-wise: fullest bucket": ("if (bucket_elems[b] < bucket_elems[best]) best = b;",
+                                   "if (bucket_elems[b] > bucket_elems[best]) best = b;"),
     "valid rows from W": ("row[4] = (H - ORA_TILE_DIM * i) < ORA_TILE_DIM ? H - ORA_TILE_DIM * i : ORA_TILE_DIM;",
                           "row[4] = (W - ORA_TILE_DIM * i) < ORA_TILE_DIM ? W - ORA_TILE_DIM * i : ORA_TILE_DIM;"),
     "fold transposes the tile": ("tile[a * ORA_TILE_DIM + b] =", "tile[b * ORA_TILE_DIM + a] ="),
@@ -72,7 +76,9 @@ def _pins():
              lambda: Q.test_zero_tile_guard_and_padding(o)]
     pins += [lambda s=s: P.test_brute_force_ownership(o, s) for s in range(4)]
     pins += [lambda: P.test_toy_walkthrough(o), lambda: P.test_workload_counts(o),
-             lambda: P.test_more_ranks_than_tiles(o)]
+             lambda: P.test_more_ranks_than_tiles(o), lambda: P.test_paramwise_graham_worst_case(o),
+             lambda: P.test_paramwise_too_few_weights(o)]
+    pins += [lambda s=s: P.test_paramwise_brute_force(o, s) for s in range(10)]
     pins += [lambda sh=sh: L.test_pack_matches_im2col(o, sh) for sh in L.SHAPES]
     pins += [lambda sh=sh: L.test_unpack_matches_col2im(o, sh) for sh in L.SHAPES]
     pins.append(lambda: L.test_round_trip_multi_param_multi_rank(o))

@@ -104,3 +104,57 @@ def test_more_ranks_than_tiles(ora):
         assert q == 1
         owned_all.append(owned)
     assert owned_all == [1, 1, 1, 1, 0, 0, 0]
+
+
+# ---- the param-wise split ----------------------------------------------------
+
+def _opt_makespan(sizes, D):
+    best = None
+    for assign in itertools.product(range(D), repeat=len(sizes)):
+        loads = [0] * D
+        for s, b in zip(sizes, assign):
+            loads[b] += s
+        m = max(loads)
+        best = m if best is None else min(best, m)
+    return best
+
+
+def test_paramwise_graham_worst_case(ora):
+    """Graham's tight example for largest-first greedy on 2 buckets (R. L.
+    Graham, "Bounds on multiprocessing timing anomalies", SIAM J. Appl. Math.
+    17, 1969): sizes 3, 3, 2, 2, 2 -- greedy reaches 7 where 6 is optimal,
+    exactly the bound 4/3 - 1/(3D) times the optimum."""
+    bop, be = ora.paramwise_split([(1, 1, s) for s in (3, 3, 2, 2, 2)], 2)
+    assert list(bop) == [0, 1, 0, 1, 0] and sorted(be) == [5, 7]
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_paramwise_brute_force(ora, seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 8))
+    D = int(rng.integers(1, 4))
+    dims = [(int(rng.integers(1, 3)), int(rng.integers(1, 20)), int(rng.integers(1, 20)))
+            for _ in range(n)]
+    sizes = [E * H * W for E, H, W in dims]
+    bop, be = ora.paramwise_split(dims, D)
+    assert ((bop >= 0) & (bop < D)).all()
+    for b in range(D):
+        assert be[b] == sum(s for s, x in zip(sizes, bop) if x == b)
+    opt = _opt_makespan(sizes, D)
+    assert opt <= be.max() <= (4 / 3 - 1 / (3 * D)) * opt + 1e-9
+    # largest first: a weight never lands on a bucket that was already the
+    # fullest when it was placed, so no bucket exceeds the rest by more than
+    # its own smallest weight
+    for b in range(D):
+        mine = [s for s, x in zip(sizes, bop) if x == b]
+        if mine:
+            assert be[b] - min(mine) <= min(be) or D == 1
+
+
+def test_paramwise_too_few_weights(ora):
+    """The page's second drawback: with fewer weights than ranks some
+    buckets stay empty, and every rank is padded to a whole weight."""
+    moe = [(256, 7168, 2048), (256, 7168, 2048), (256, 2048, 7168)]
+    bop, be = ora.paramwise_split(moe, 32)
+    assert sorted(bop) == [0, 1, 2] and (be == 0).sum() == 29
+    assert be.max() == 256 * 7168 * 2048
