@@ -197,6 +197,67 @@ def test_full_model_unfold_after_allgather():
         assert torch.equal(sc[p], wantsc[p]), p
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_random_configurations(seed):
+    """Random ragged weights, D, rank, hyper-parameters (weight decay 0 or
+    not, large eps, step counters up to 10^6) and value scales, inputs drawn
+    on the host with numpy; every slot of every entry point vs the oracle."""
+    rng = np.random.default_rng(1000 + seed)
+    dims = [(int(rng.integers(1, 3)), int(rng.integers(1, 400)), int(rng.integers(1, 400)))
+            for _ in range(int(rng.integers(1, 5)))]
+    D = int(rng.integers(1, 5))
+    rank = int(rng.integers(0, D))
+    hp = dict(lr=float(10 ** rng.uniform(-5, -1)), beta1=float(rng.choice([0.0, 0.5, 0.9])),
+              beta2=float(rng.choice([0.9, 0.95, 0.999])), eps=float(10 ** rng.uniform(-10, -3)),
+              weight_decay=float(rng.choice([0.0, 0.01, 0.3])))
+    t = int(rng.choice([1, 2, 57, 10 ** 6]))
+    _say("random config seed", 1000 + seed, "dims", dims, "D", D, "rank", rank, "hp", hp, "t", t)
+    q, owned, table = oracle.plan(dims, D, rank)
+    scale = float(10 ** rng.uniform(-4, 1))
+    host = {k: [rng.normal(0, s, d).astype(np.float32) for d in dims]
+            for k, s in (("p", scale), ("g", scale * 1e-2), ("m", scale * 1e-3))}
+    host["v"] = [np.square(rng.normal(0, scale * 1e-2, d)).astype(np.float32) for d in dims]
+    ora_state = {k: oracle.pack(dims, host[k], table) for k in ("p", "g", "m", "v")}
+    codes_o, scale_o, near_o = oracle.step(ora_state["p"], ora_state["g"], ora_state["m"],
+                                           ora_state["v"], oracle.hparams(step=t, **hp))
+    plan = bfz.Plan(dims, D, rank)
+    dev = {k: [torch.from_numpy(x.reshape(-1)).cuda() for x in host[k]] for k in host}
+    for route in ("unfused", "fused", "fused_unpack"):
+        st = {}
+        for k in ("p", "m", "v"):
+            st[k] = torch.empty(q * 16384, dtype=torch.float32, device="cuda")
+            bfz.pack_shard(plan, dev[k], st[k])
+        codes = torch.empty(q * 16384, dtype=torch.uint8, device="cuda")
+        sc = torch.empty(q, dtype=torch.float32, device="cuda")
+        h = bfz.AdamW(step=t, **hp)
+        if route == "unfused":
+            gt = torch.empty(q * 16384, dtype=torch.float32, device="cuda")
+            bfz.pack_shard(plan, dev["g"], gt)
+            bfz.adamw_fp8_step(st["p"], gt, st["m"], st["v"], codes, sc, h)
+        elif route == "fused":
+            bfz.fold_adamw_fp8_step(plan, dev["g"], st["p"], st["m"], st["v"], codes, sc, h)
+        else:
+            d8 = [torch.zeros(int(np.prod(d)), dtype=torch.uint8, device="cuda") for d in dims]
+            dsc = [torch.zeros(d[0] * -(-d[1] // 128) * -(-d[2] // 128), dtype=torch.float32,
+                               device="cuda") for d in dims]
+            bfz.fold_adamw_fp8_step_unpack(plan, dev["g"], st["p"], st["m"], st["v"], codes, sc,
+                                           d8, dsc, h)
+        torch.cuda.synchronize()
+        gpu = dict(master=st["p"].cpu().numpy(), m=st["m"].cpu().numpy(), v=st["v"].cpu().numpy(),
+                   codes=codes.cpu().numpy(), scale_inv=sc.cpu().numpy())
+        ora = dict(master=ora_state["p"], m=ora_state["m"], v=ora_state["v"], codes=codes_o,
+                   scale_inv=scale_o, near=near_o)
+        rep = _check(gpu, ora, f"random seed {1000 + seed} {route}")
+        assert rep["exact"]
+        if route == "fused_unpack":
+            o8 = [np.zeros(d, dtype=np.uint8) for d in dims]
+            osc = [np.zeros((d[0], -(-d[1] // 128), -(-d[2] // 128)), dtype=np.float32) for d in dims]
+            oracle.unpack(dims, codes_o, scale_o, table, o8, osc)
+            for k in range(len(dims)):
+                assert np.array_equal(d8[k].cpu().numpy(), o8[k].reshape(-1)), k
+                assert np.array_equal(dsc[k].cpu().numpy(), osc[k].reshape(-1)), k
+
+
 def test_amax_at_every_position():
     """16384 tiles; tile k has its largest |value| at element k (sign
     alternating).  lr = 0 leaves the master unchanged, so the scale must be
