@@ -144,6 +144,44 @@ def cpu_baseline(w, target_s=10.0):
             "seconds": round(dt, 2)}
 
 
+def time_transpose(g, t, steps, stream):
+    """One power-of-two step (so every tile scale is a power of two), then
+    bfz_transpose_pow2 of the shard timed over `steps` launches: W^T codes
+    and per-group power-of-two scales by exponent edits."""
+    import torch
+
+    import blockwise_fp8_zero_amd as bfz
+    pow2_was = g.pow2
+    g.pow2 = True
+    g.apply(t)
+    g.pow2 = pow2_was
+    dims = g.w.dims
+    dt = [None] * len(dims)
+    ds = [None] * len(dims)
+    for p in g.touched:
+        E, H, W = dims[p]
+        dt[p] = torch.empty(E * W * H, dtype=torch.uint8, device="cuda")
+        ds[p] = torch.empty(E * W * (-(-H // 128)), dtype=torch.float32, device="cuda")
+    bfz.transpose_pow2(g.plan, g.codes, g.scale_inv, dt, ds)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        bfz.transpose_pow2(g.plan, g.codes, g.scale_inv, dt, ds)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    owned = g.table[:g.owned]
+    valid = int((owned[:, 4] * owned[:, 5]).sum())
+    # read: tile codes + scale; write: W^T codes of the valid elements + one
+    # scale per valid column of every owned tile
+    algo = g.q * bfz.TILE_ELEMS + 4 * g.q + valid + 4 * int(owned[:, 5].sum())
+    del dt, ds
+    return {"kernel": "transpose_pow2_kernel", "ms": ms, "algorithmic_bytes": algo,
+            "GBps": algo / (ms * 1e-3) / 1e9, "frac": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,6 +192,10 @@ def main():
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--path", default="fused_unpack", choices=list(KERNEL_OF_PATH),
                     help="which entry points make up a step (see the module docstring)")
+    ap.add_argument("--pow2", action="store_true",
+                    help="power-of-two tile scales in the timed steps (bfz_adamw.scale_pow2)")
+    ap.add_argument("--skip-transpose", action="store_true",
+                    help="do not time bfz_transpose_pow2 after the steps")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -170,7 +212,7 @@ def main():
     w = WL.BY_NAME[args.workload]()
     log(f"workload {w.name}: {w.description}")
     t0 = time.perf_counter()
-    g = GpuWorkload(w, mode=args.path)
+    g = GpuWorkload(w, mode=args.path, pow2=args.pow2)
     g.load_state()
     prior = w.steps[:-1]
     if prior:
@@ -241,6 +283,10 @@ def main():
     if args.path == "unfused":
         whole_bytes += PACK_BYTES_PER_ELEM * elems
     traffic = measured_traffic(kernel) if w.name == "dense_llm" else None
+    transpose = None
+    if not args.skip_transpose:
+        transpose = time_transpose(g, t_next, args.steps, stream)
+
     out = {
         "metric": METRIC,
         "value": elems / (ms_per_step * 1e-3),
@@ -281,6 +327,7 @@ def main():
             "algorithmic_bytes_per_launch": algo_bytes,
         },
         "cpu_baseline": None,
+        "transpose_pow2": transpose,
     }
     if not args.skip_cpu_baseline:
         log("cpu baseline (oracle) ...")

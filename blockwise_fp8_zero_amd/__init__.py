@@ -25,9 +25,11 @@ class BfzError(RuntimeError):
 
 
 class AdamW(C.Structure):
-    """Hyper-parameters of one step; step is the counter t >= 1."""
+    """Hyper-parameters of one step; step is the counter t >= 1; scale_pow2
+    selects power-of-two tile scales."""
     _fields_ = [("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
-                ("eps", C.c_double), ("weight_decay", C.c_double), ("step", C.c_int64)]
+                ("eps", C.c_double), ("weight_decay", C.c_double), ("step", C.c_int64),
+                ("scale_pow2", C.c_int32)]
 
 
 _lib = None
@@ -58,6 +60,7 @@ def lib():
         L.fold_adamw_fp8_step_unpack.argtypes = [P, P, P, P, P, P, P, P, P, C.POINTER(AdamW), P]
         L.unpack_fp8.argtypes = [P, P, P, P, P, P]
         L.bfz_e4m3_encode.argtypes = [P, P, i64, P]
+        L.bfz_transpose_pow2.argtypes = [P, P, P, P, P, P]
         L.bfz_last_error.argtypes = []
         L.bfz_last_error.restype = C.c_char_p
         _lib = L
@@ -242,6 +245,20 @@ def unpack_fp8(plan: Plan, codes, scale_inv, dst_fp8, dst_scale, stream=None):
     _check(lib().unpack_fp8(plan.handle, _dev(codes, torch.uint8, "codes", q * TILE_ELEMS),
                             _dev(scale_inv, torch.float32, "scale_inv", q),
                             C.cast(a8, C.c_void_p), C.cast(asc, C.c_void_p), _stream(stream)))
+
+
+def transpose_pow2(plan: Plan, codes, scale_inv, dst_t, dst_t_scale, stream=None):
+    """Transposed copy of the shard's power-of-two-quantized tiles by exponent
+    edits: dst_t[p] uint8 (E, W, H), dst_t_scale[p] float32 (E, W, ceil(H/128))."""
+    import torch
+    n = len(plan.dims)
+    q = plan.shard_tiles
+    a8 = _ptr_array(dst_t, torch.uint8, "dst_t", n)
+    asc = _ptr_array(dst_t_scale, torch.float32, "dst_t_scale", n)
+    _check(lib().bfz_transpose_pow2(plan.handle, _dev(codes, torch.uint8, "codes", q * TILE_ELEMS),
+                                    _dev(scale_inv, torch.float32, "scale_inv", q),
+                                    C.cast(a8, C.c_void_p), C.cast(asc, C.c_void_p),
+                                    _stream(stream)))
 
 
 def e4m3_encode(x, out, stream=None):

@@ -113,6 +113,7 @@ int make_scalars(const bfz_adamw* hp, StepScalars* s, const char* where) {
     s->eps = float(eps);
     s->decay = float(lr * wd);
     s->has_decay = wd != 0.0;
+    s->pow2 = hp->scale_pow2 != 0;
     return BFZ_OK;
 }
 
@@ -214,6 +215,37 @@ extern "C" int fold_adamw_fp8_step_unpack(const bfz_plan* plan, const float* con
                                           master + off, m + off, v + off,
                                           codes ? codes + off : nullptr,
                                           scale_inv ? scale_inv + seg.slot0 : nullptr, s, stream);
+        if (err != hipSuccess) return hip_fail(where, err);
+    }
+    return BFZ_OK;
+}
+
+extern "C" int bfz_transpose_pow2(const bfz_plan* plan, const uint8_t* codes,
+                                  const float* scale_inv, uint8_t* const* dst_t,
+                                  float* const* dst_t_scale, void* stream) {
+    const char* where = "bfz_transpose_pow2";
+    if (!plan || !codes || !scale_inv || !dst_t || !dst_t_scale)
+        return fail(BFZ_EINVAL, "%s: null pointer", where);
+    if (!plan->d_entries) return fail(BFZ_ESTATE, "%s: plan not uploaded (bfz_plan_upload)", where);
+    if (!aligned(codes, 16)) return fail(BFZ_EALIGN, "%s: codes must be 16-byte aligned", where);
+    if (!aligned(scale_inv, 4)) return fail(BFZ_EALIGN, "%s: scale_inv must be 4-byte aligned", where);
+    int rc = check_weights(plan, reinterpret_cast<const void* const*>(dst_t), where);
+    if (!rc) rc = check_weights(plan, reinterpret_cast<const void* const*>(dst_t_scale), where);
+    if (rc) return rc;
+    for (int32_t w = 0; w < plan->n_weights; ++w)
+        if (dst_t_scale[w] && !aligned(dst_t_scale[w], 4))
+            return fail(BFZ_EALIGN, "%s: scale grid %d must be 4-byte aligned", where, w);
+    for (const Segment& seg : plan->segments) {
+        if (seg.n_weights == 0) continue;
+        TransposeArgs args{};
+        for (int32_t k = 0; k < seg.n_weights; ++k) {
+            args.codes[k] = dst_t[seg.weight0 + k];
+            args.scale[k] = dst_t_scale[seg.weight0 + k];
+            args.rows[k] = int32_t(plan->dims[3 * (seg.weight0 + k) + 1]);
+        }
+        int err = launch_transpose_pow2(plan->d_entries + seg.slot0, seg.n_slots,
+                                        codes + seg.slot0 * kTileElems, scale_inv + seg.slot0,
+                                        args, stream);
         if (err != hipSuccess) return hip_fail(where, err);
     }
     return BFZ_OK;

@@ -43,10 +43,17 @@ struct UnpackArgs {
     float* scale[kSegWeights];
 };
 
+struct TransposeArgs {
+    uint8_t* codes[kSegWeights];  // W^T, row-major [E, W, H]
+    float* scale[kSegWeights];    // [E, W, ceil(H / 128)]
+    int32_t rows[kSegWeights];    // H of each weight
+};
+
 // FP32 scalars of one AdamW step, rounded once from double.
 struct StepScalars {
     float b1, c1, b2, c2, step_size, sbc2, eps, decay;
     int32_t has_decay;
+    int32_t pow2;  // power-of-two tile scales
 };
 
 // Kernel launchers (kernels.hip).  They return a hipError_t value as int.
@@ -62,6 +69,8 @@ int launch_fold_step(const TileEntry* d_entries, int64_t n_slots, const PackArgs
 int launch_fold_step_unfold(const TileEntry* d_entries, int64_t n_slots, const PackArgs& grads,
                             const UnpackArgs& outs, float* master, float* m, float* v,
                             uint8_t* codes, float* scale_inv, const StepScalars& s, void* stream);
+int launch_transpose_pow2(const TileEntry* d_entries, int64_t n_slots, const uint8_t* codes,
+                          const float* scale_inv, const TransposeArgs& args, void* stream);
 int launch_encode(const float* in, uint8_t* out, int64_t n, void* stream);
 const char* hip_error_string(int err);
 

@@ -44,6 +44,27 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
     return code | sign;
 }
 
+// Power-of-two tile scale: the smallest 2^T with 448 * 2^T >= amax (amax
+// finite, > 0), T clamped to >= -149 (the smallest binary32 power of two).
+// With amax = (1 + f) 2^e and 448 = 1.75 * 2^8: T = e - 8 when 1 + f <= 1.75,
+// else e - 7.  Exact integer work on the bits.
+__device__ __forceinline__ float pow2_scale(float amax) {
+    const uint32_t b = __float_as_uint(amax);
+    int e;
+    uint32_t mant;
+    if (b >= 0x00800000u) {
+        e = (int)(b >> 23) - 127;
+        mant = b & 0x7FFFFFu;
+    } else {  // subnormal amax = b * 2^-149
+        const int lead = 31 - __clz(b);
+        e = lead - 149;
+        mant = (b << (23 - lead)) & 0x7FFFFFu;
+    }
+    int T = e - 8 + (mant > 0x600000u ? 1 : 0);
+    if (T < -149) T = -149;
+    return T >= -126 ? __uint_as_float((uint32_t)(T + 127) << 23) : __uint_as_float(1u << (T + 149));
+}
+
 // AdamW of one element, the update of the Int8AdamW step (lpnh.cn essay,
 // section 4.3): moments, bias-corrected denominator, step, then decay of
 // the updated value.
@@ -203,9 +224,10 @@ __device__ __forceinline__ void step_tile(int64_t tile, float* __restrict__ mast
 #pragma unroll
     for (int w = 1; w < kStepWaves; ++w) amax = fmaxf(amax, wave_amax[w]);
 
-    // scale_inv = amax / 448; an all-zero tile takes 1 and codes 0.
+    // scale_inv = amax / 448 (or its power-of-two form); an all-zero tile
+    // takes 1 and codes 0.
     const bool zero = amax == 0.0f;
-    const float scale = zero ? 1.0f : amax / 448.0f;
+    const float scale = zero ? 1.0f : (s.pow2 ? pow2_scale(amax) : amax / 448.0f);
     if (threadIdx.x == 0) {
         if (scale_inv) scale_inv[tile] = scale;
         if (out.scale_cell) *out.scale_cell = scale;
@@ -339,6 +361,131 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const TileEntry* __res
     if (threadIdx.x == 0) args.scale[t.local][t.scale_index] = scale_inv[slot];
 }
 
+// ---------------------------------------------------------------------
+// Scaling-aware transpose of power-of-two-quantized tiles: exponent edits.
+// ---------------------------------------------------------------------
+
+// Doublings the E4M3 magnitude code `mag` (1..126) can take and stay within
+// 448: a normal code (E, M) has 15 - E of them (14 - E when M = 7, since
+// 1.875 * 2 > 1.75); subnormals M * 2^-9 have 17 (M = 1), 16 (M = 2, 3) or
+// 15 (M = 4..7).
+__device__ __forceinline__ int e4m3_headroom(uint32_t mag) {
+    if (mag >= 8u) return ((mag & 7u) == 7u ? 14 : 15) - (int)(mag >> 3);
+    return mag == 1u ? 17 : (mag < 4u ? 16 : 15);
+}
+
+// The code of the same value on a scale 2^d times finer: d doublings.  A
+// subnormal doubles by shifting its 3-bit significand left until it turns
+// normal (code 8 = 2^-6 is exactly 4 * 2^-9 doubled); a normal doubles by
+// adding 1 to its exponent field (+8).  Exact while within 448, which the
+// caller's headroom guarantees.
+__device__ __forceinline__ uint32_t e4m3_scale_up(uint32_t code, int d) {
+    const uint32_t sign = code & 0x80u;
+    uint32_t mag = code & 0x7Fu;
+    if (mag == 0u) return code;
+    if (mag < 8u) {
+        const int sh = min(d, 4 - (32 - __clz(mag)));
+        mag <<= sh;
+        d -= sh;
+    }
+    return sign | (mag + ((uint32_t)d << 3));
+}
+
+// binary32 exponent of a power of two (normal or subnormal).
+__device__ __forceinline__ int pow2_exponent(float s) {
+    const uint32_t b = __float_as_uint(s);
+    return b >= 0x00800000u ? (int)(b >> 23) - 127 : (31 - __clz(b)) - 149;
+}
+
+__device__ __forceinline__ float pow2_value(int T) {
+    return T >= -126 ? __uint_as_float((uint32_t)(T + 127) << 23) : __uint_as_float(1u << (T + 149));
+}
+
+// One 256-thread workgroup per owned slot.
+//  1. Thread t reads 4x4-byte blocks of the tile (block column t % 32, block
+//     rows t / 32 + 8 m), transposes each in registers and writes its four
+//     columns to LDS as words of W^T rows: W^T row c (= tile column c) holds
+//     bytes r = 0..127 (= tile rows).  Word w of row c sits at c * 32 +
+//     ((w + c / 4) % 32), a rotation that spreads a wave's writes over all
+//     32 banks.
+//  2. Eight consecutive lanes own one W^T row, 16 bytes each, so a wave
+//     stores eight contiguous 128-byte row segments.  The group's largest
+//     magnitude code (valid rows only) is an 8-lane shuffle reduction; it
+//     gives the headroom d (clamped so 2^(T - d) >= 2^-149), every code is
+//     moved up d binades, and lane 0 of the row writes the group scale.
+// An all-zero column: scale 1, codes 0.
+__global__ __launch_bounds__(kThreads) void transpose_pow2_kernel(
+    const TileEntry* __restrict__ entries, const uint8_t* __restrict__ codes,
+    const float* __restrict__ scale_inv, TransposeArgs args) {
+    __shared__ uint32_t tile_t[kTileDim * 32];
+    const int64_t slot = blockIdx.x;
+    const TileEntry t = entries[slot];
+    if (t.local < 0) return;
+    const uint32_t* in = reinterpret_cast<const uint32_t*>(codes + slot * kTileElems);
+    const int bc = threadIdx.x & 31;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+        const int br = (threadIdx.x >> 5) + 8 * mb;
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = in[(4 * br + k) * 32 + bc];
+#pragma unroll
+        for (int l = 0; l < 4; ++l) {
+            const uint32_t col = ((w[0] >> (8 * l)) & 0xFFu) | (((w[1] >> (8 * l)) & 0xFFu) << 8) |
+                                 (((w[2] >> (8 * l)) & 0xFFu) << 16) |
+                                 (((w[3] >> (8 * l)) & 0xFFu) << 24);
+            const int c = 4 * bc + l;
+            tile_t[c * 32 + ((br + bc) & 31)] = col;  // rotation: (br + c / 4) % 32
+        }
+    }
+    __syncthreads();
+
+    const int T = pow2_exponent(scale_inv[slot]);
+    const int64_t H = args.rows[t.local], W = t.ld;
+    const int64_t hb = (H + kTileDim - 1) / kTileDim, wb = (W + kTileDim - 1) / kTileDim;
+    const int64_t j = t.scale_index % wb, ei = t.scale_index / wb;
+    const int64_t i = ei % hb, e = ei / hb;
+    const int k2 = threadIdx.x & 7;        // 16-byte chunk of the row: rows 16 k2 .. +15
+    const int r0 = 16 * k2;
+#pragma unroll
+    for (int mr = 0; mr < 4; ++mr) {
+        const int c = (threadIdx.x >> 3) + 32 * mr;  // W^T row within the tile
+        uint32_t v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = tile_t[c * 32 + ((4 * k2 + q + c / 4) & 31)];
+        // valid rows of this chunk, then the row's largest magnitude code
+        const int nvalid = max(0, min(16, (int)t.valid_rows - r0));
+        uint32_t mx = 0;
+#pragma unroll
+        for (int l = 0; l < 16; ++l)
+            if (l < nvalid) mx = max(mx, (v[l >> 2] >> (8 * (l & 3))) & 0x7Fu);
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1, 64));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2, 64));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 4, 64));
+        if (c >= t.valid_cols) continue;
+        int d = mx == 0u ? 0 : e4m3_headroom(mx);
+        if (T - d < -149) d = T + 149;
+        const int64_t out_row = e * W + kTileDim * j + c;
+        if (k2 == 0) args.scale[t.local][out_row * hb + i] = mx == 0u ? 1.0f : pow2_value(T - d);
+        if (nvalid == 0) continue;
+        uint32_t o[4] = {0u, 0u, 0u, 0u};
+        if (mx != 0u) {
+#pragma unroll
+            for (int l = 0; l < 16; ++l)
+                o[l >> 2] |= (l < nvalid ? e4m3_scale_up((v[l >> 2] >> (8 * (l & 3))) & 0xFFu, d) : 0u)
+                             << (8 * (l & 3));
+        }
+        uint8_t* q = args.codes[t.local] + out_row * H + kTileDim * i + r0;
+        if (nvalid == 16 && (reinterpret_cast<uintptr_t>(q) & 15u) == 0) {
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 y = {o[0], o[1], o[2], o[3]};
+            __builtin_nontemporal_store(y, reinterpret_cast<u32x4*>(q));
+        } else {
+            for (int l = 0; l < nvalid; ++l) q[l] = (uint8_t)(o[l >> 2] >> (8 * (l & 3)));
+        }
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void encode_kernel(const float* __restrict__ in,
                                                           uint8_t* __restrict__ out, int64_t n) {
     const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -417,6 +564,14 @@ int launch_unpack(const TileEntry* d_entries, int64_t n_slots, const uint8_t* co
                   const float* scale_inv, const UnpackArgs& args, void* stream) {
     if (n_slots == 0) return hipSuccess;
     hipLaunchKernelGGL(unpack_kernel, dim3((uint32_t)n_slots), dim3(kThreads), 0,
+                       (hipStream_t)stream, d_entries, codes, scale_inv, args);
+    return hipGetLastError();
+}
+
+int launch_transpose_pow2(const TileEntry* d_entries, int64_t n_slots, const uint8_t* codes,
+                          const float* scale_inv, const TransposeArgs& args, void* stream) {
+    if (n_slots == 0) return hipSuccess;
+    hipLaunchKernelGGL(transpose_pow2_kernel, dim3((uint32_t)n_slots), dim3(kThreads), 0,
                        (hipStream_t)stream, d_entries, codes, scale_inv, args);
     return hipGetLastError();
 }

@@ -56,10 +56,16 @@ typedef struct bfz_plan bfz_plan;
 
 /* AdamW hyper-parameters.  step is the counter t >= 1 of the step being
  * taken (the first step is t = 1).  Requires lr, eps, weight_decay finite,
- * eps >= 0, 0 <= beta1 < 1, 0 <= beta2 < 1. */
+ * eps >= 0, 0 <= beta1 < 1, 0 <= beta2 < 1.
+ * scale_pow2 = 0: scale_inv = amax / 448.  scale_pow2 != 0: scale_inv is
+ * the smallest power of two 2^T with 448 * 2^T >= amax (T >= -149), so
+ * every quotient p / scale_inv is exact and codes can later be moved
+ * between scales by exponent edits alone ("FP8-Flow-MoE", section 3.1;
+ * see bfz_transpose_pow2). */
 typedef struct {
     double lr, beta1, beta2, eps, weight_decay;
     int64_t step;
+    int32_t scale_pow2;
 } bfz_adamw;
 
 /*
@@ -141,7 +147,8 @@ int pack_shard(const bfz_plan* plan, const float* const* src, float* dst, void* 
  *                       v = b2 v + (1 - b2) g^2
  *                       p = p - (lr / (1 - b1^t)) m / (sqrt(v) / sqrt(1 - b2^t) + eps)
  *                       p = p - lr wd p          (when wd != 0; on the updated p)
- *   per tile:           amax = max |p|;  scale_inv = amax / 448, or 1 when amax == 0
+ *   per tile:           amax = max |p|;  scale_inv = amax / 448 (or its power-of-two
+ *                       form, see bfz_adamw.scale_pow2), or 1 when amax == 0
  *   per element:        code = E4M3(p / scale_inv), 0 in an all-zero tile,
  * where E4M3 is round-to-nearest (ties to even) onto the OCP E4M3FN values,
  * saturating at +-448, keeping the sign (tiny negatives give 0x80).
@@ -215,6 +222,30 @@ int fold_adamw_fp8_step_unpack(const bfz_plan* plan, const float* const* grad, f
  */
 int unpack_fp8(const bfz_plan* plan, const uint8_t* codes, const float* scale_inv,
                uint8_t* const* dst_fp8, float* const* dst_scale, void* stream);
+
+/*
+ * Scaling-aware transpose ("FP8-Flow-MoE", section 3.1, direct transpose):
+ * the transposed copy W^T of the rank's tiles, re-quantized by exponent
+ * edits only.  Input: codes and scales of a step run with scale_pow2 (every
+ * scale_inv a power of two; other scales give unspecified results).
+ * Output, for every owned tile (i, j) of weight p, expert e:
+ *   dst_t[p][e][128 j + c][128 i + r]   (W^T, row-major [E, W, H])
+ *     = code of the tile's value at (r, c), re-expressed on the scale
+ *   dst_t_scale[p][e][128 j + c][i]     ([E, W, ceil(H/128)])
+ * which is the smallest power of two holding that 128-element group of the
+ * W^T row (the tile rule applied to the group; >= 2^-149).  The group scale
+ * never exceeds the tile's, so the edits only raise exponents: every value
+ * is reproduced exactly, with none of the extra rounding a dequantize ->
+ * transpose -> quantize pass with arbitrary scales would add.  An all-zero
+ * group gets scale 1 and codes 0.  codes: q * 16384 bytes (16-byte
+ * aligned); scale_inv: q floats; dst_t / dst_t_scale: host arrays of
+ * n_params device pointers (NULL allowed for weights the rank does not
+ * touch; any alignment for dst_t, 4 bytes for dst_t_scale).  Asynchronous
+ * on `stream`; no allocation.
+ * Errors: BFZ_EINVAL, BFZ_EALIGN, BFZ_ESTATE, BFZ_EHIP.
+ */
+int bfz_transpose_pow2(const bfz_plan* plan, const uint8_t* codes, const float* scale_inv,
+                       uint8_t* const* dst_t, float* const* dst_t_scale, void* stream);
 
 /*
  * The E4M3 rounding adamw_fp8_step applies to p / scale_inv, exposed on

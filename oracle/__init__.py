@@ -53,6 +53,12 @@ def lib():
         L.ora_adamw.argtypes = [P, P, P, P, C.c_int64, C.POINTER(HParams)]
         L.ora_quant_tiles.argtypes = [P, C.c_int64, P, P, P, C.c_double]
         L.ora_step.argtypes = [P, P, P, P, C.c_int64, C.POINTER(HParams), P, P, P, C.c_double]
+        L.ora_transpose_pow2.argtypes = [P, C.c_int32, P, P, P, C.c_int64, P, P]
+        L.ora_pow2_scale.argtypes = [C.c_float]
+        L.ora_pow2_scale.restype = C.c_float
+        L.ora_quant_tiles_mode.argtypes = [P, C.c_int64, P, P, P, C.c_double, C.c_int]
+        L.ora_step_mode.argtypes = [P, P, P, P, C.c_int64, C.POINTER(HParams), P, P, P, C.c_double,
+                                    C.c_int]
         _lib = L
     return _lib
 
@@ -164,6 +170,24 @@ def unpack(dims, codes, scale_inv, table, dst_codes, dst_scale):
                      table.shape[0], C.cast(pc, C.c_void_p), C.cast(ps, C.c_void_p))
 
 
+def transpose_pow2(dims, codes, scale_inv, table, dst_t, dst_t_scale):
+    """dst_t / dst_t_scale: per-param uint8 (E, W, H) / float32 (E, W, ceil(H/128))
+    arrays (or None), written for the owned slots."""
+    d = _dims_array(dims)
+    _need(codes, np.uint8, "codes")
+    _need(scale_inv, np.float32, "scale_inv")
+    table = np.ascontiguousarray(table, dtype=np.int64)
+    n = max(1, d.shape[0])
+    pc = (C.c_void_p * n)()
+    ps = (C.c_void_p * n)()
+    for k in range(d.shape[0]):
+        if dst_t[k] is not None:
+            pc[k] = _need(dst_t[k], np.uint8, "dst_t").ctypes.data
+            ps[k] = _need(dst_t_scale[k], np.float32, "dst_t_scale").ctypes.data
+    lib().ora_transpose_pow2(_ptr(d), d.shape[0], _ptr(codes), _ptr(scale_inv), _ptr(table),
+                             table.shape[0], C.cast(pc, C.c_void_p), C.cast(ps, C.c_void_p))
+
+
 # ---- AdamW, quant, step ---------------------------------------------------
 def adamw(p, g, m, v, hp: HParams):
     """In place on float32 arrays of equal size."""
@@ -173,7 +197,11 @@ def adamw(p, g, m, v, hp: HParams):
     lib().ora_adamw(_ptr(p), _ptr(g), _ptr(m), _ptr(v), p.size, C.byref(hp))
 
 
-def quant_tiles(p, rel: float = 1e-6):
+def pow2_scale(amax: float) -> float:
+    return float(lib().ora_pow2_scale(amax))
+
+
+def quant_tiles(p, rel: float = 1e-6, pow2: bool = False):
     """Returns (codes uint8 [n], scale_inv float32 [n_tiles], near_mid uint8 [n])."""
     _need(p, np.float32, "p")
     assert p.size % TILE_ELEMS == 0
@@ -181,11 +209,11 @@ def quant_tiles(p, rel: float = 1e-6):
     codes = np.empty(p.size, dtype=np.uint8)
     scale = np.empty(nt, dtype=np.float32)
     near = np.empty(p.size, dtype=np.uint8)
-    lib().ora_quant_tiles(_ptr(p), nt, _ptr(codes), _ptr(scale), _ptr(near), rel)
+    lib().ora_quant_tiles_mode(_ptr(p), nt, _ptr(codes), _ptr(scale), _ptr(near), rel, int(pow2))
     return codes, scale, near
 
 
-def step(p, g, m, v, hp: HParams, rel: float = 1e-6):
+def step(p, g, m, v, hp: HParams, rel: float = 1e-6, pow2: bool = False):
     """Fused reference step in place on p, m, v; returns (codes, scale_inv, near_mid)."""
     for a, nme in ((p, "p"), (g, "g"), (m, "m"), (v, "v")):
         _need(a, np.float32, nme)
@@ -194,6 +222,6 @@ def step(p, g, m, v, hp: HParams, rel: float = 1e-6):
     codes = np.empty(p.size, dtype=np.uint8)
     scale = np.empty(nt, dtype=np.float32)
     near = np.empty(p.size, dtype=np.uint8)
-    lib().ora_step(_ptr(p), _ptr(g), _ptr(m), _ptr(v), nt, C.byref(hp), _ptr(codes),
-                   _ptr(scale), _ptr(near), rel)
+    lib().ora_step_mode(_ptr(p), _ptr(g), _ptr(m), _ptr(v), nt, C.byref(hp), _ptr(codes),
+                        _ptr(scale), _ptr(near), rel, int(pow2))
     return codes, scale, near

@@ -257,6 +257,57 @@ void ora_unpack(const int64_t* dims, int32_t n_params, const uint8_t* codes,
     }
 }
 
+/*
+ * [FP8-Flow, §3.1, direct transpose]: with power-of-two scales a tensor
+ * quantized in one grouping can be re-expressed in another by exponent
+ * edits, so the transposed copy the backward pass needs carries no second
+ * rounding.  What it computes, written as the naive route (dequantize,
+ * transpose, quantize again): the tile's values v = dec(code) * 2^T; each
+ * 128-element group of a W^T row -- one column of the tile, its valid
+ * rows -- gets the power-of-two scale of its own amax (ora_pow2_scale, the
+ * tile rule; an all-zero group gets 1 and codes +0) and its values are
+ * encoded again.  Everything here is exact in double; the claim that the
+ * result equals the codes moved by exponent edits is what the GPU kernel
+ * is checked against.
+ * Parity: pinned in tests/test_oracle_transpose.py (lossless values,
+ * torch's own dequantize/transpose/quantize route, tight group scales).
+ */
+static double pow2_scale_d(double amax) {
+    int T = -149;
+    while (ldexp(448.0, T) < amax) ++T;
+    return ldexp(1.0, T);
+}
+
+void ora_transpose_pow2(const int64_t* dims, int32_t n_params, const uint8_t* codes,
+                        const float* scale_inv, const int64_t* table, int64_t q,
+                        uint8_t* const* dst_t, float* const* dst_t_scale) {
+    (void)n_params;
+    for (int64_t s = 0; s < q; ++s) {
+        const int64_t* row = table + 6 * s;
+        if (row[0] < 0) continue;
+        int64_t p = row[0], e = row[1], i = row[2], j = row[3], vr = row[4], vc = row[5];
+        int64_t H = dims[3 * p + 1], W = dims[3 * p + 2];
+        int64_t hb = ceil_div(H, ORA_TILE_DIM);
+        const uint8_t* tile = codes + s * ORA_TILE_ELEMS;
+        double tile_scale = (double)scale_inv[s];
+        for (int64_t c = 0; c < vc; ++c) {
+            double amax = 0.0;
+            for (int64_t r = 0; r < vr; ++r) {
+                double v = fabs(ora_e4m3_decode(tile[r * ORA_TILE_DIM + c]) * tile_scale);
+                if (v > amax) amax = v;
+            }
+            int64_t out_row = e * W + ORA_TILE_DIM * j + c;  /* row of W^T */
+            double g = amax == 0.0 ? 1.0 : pow2_scale_d(amax);
+            dst_t_scale[p][out_row * hb + i] = (float)g;
+            for (int64_t r = 0; r < vr; ++r) {
+                double v = ora_e4m3_decode(tile[r * ORA_TILE_DIM + c]) * tile_scale;
+                uint8_t code = amax == 0.0 ? 0 : ora_e4m3_encode((float)(v / g));
+                dst_t[p][out_row * H + ORA_TILE_DIM * i + r] = code;
+            }
+        }
+    }
+}
+
 /* ===================================================================== *
  * AdamW                                                                  *
  * ===================================================================== */
@@ -331,8 +382,24 @@ void ora_adamw(float* p, const float* g, float* m, float* v, int64_t n,
  * Parity: pinned by invariants (max code = 448, error bound, idempotence,
  * zero tiles) and hand-built tiles in tests/test_oracle_quant.py.
  */
-void ora_quant_tiles(const float* p, int64_t n_tiles, uint8_t* codes,
-                     float* scale_inv, uint8_t* near_mid, double rel) {
+/*
+ * [FP8-Flow, §3.1]: when every scale is a power of two, moving codes from
+ * one scale to another is a change of exponent bits only.  The power-of-two
+ * tile scale taken here is the smallest 2^T that still holds the tile:
+ * 448 * 2^T >= amax (a reading: rounding the scale up keeps every quotient
+ * within +-448, so nothing saturates).  T stops at -149, the smallest
+ * binary32 power of two.
+ * Parity: pinned in tests/test_oracle_quant.py (power of two, tight,
+ * max code in (224, 448], exact-grid tiles).
+ */
+float ora_pow2_scale(float amax) {
+    int T = -149;
+    while (ldexp(448.0, T) < (double)amax) ++T;
+    return (float)ldexp(1.0, T);
+}
+
+void ora_quant_tiles_mode(const float* p, int64_t n_tiles, uint8_t* codes,
+                          float* scale_inv, uint8_t* near_mid, double rel, int pow2) {
     for (int64_t t = 0; t < n_tiles; ++t) {
         const float* x = p + t * ORA_TILE_ELEMS;
         uint8_t* c = codes + t * ORA_TILE_ELEMS;
@@ -348,7 +415,7 @@ void ora_quant_tiles(const float* p, int64_t n_tiles, uint8_t* codes,
             }
             continue;
         }
-        float s = amax / 448.0f;
+        float s = pow2 ? ora_pow2_scale(amax) : amax / 448.0f;
         scale_inv[t] = s;
         for (int64_t k = 0; k < ORA_TILE_ELEMS; ++k) {
             float y = x[k] / s;
@@ -358,11 +425,22 @@ void ora_quant_tiles(const float* p, int64_t n_tiles, uint8_t* codes,
     }
 }
 
+void ora_quant_tiles(const float* p, int64_t n_tiles, uint8_t* codes,
+                     float* scale_inv, uint8_t* near_mid, double rel) {
+    ora_quant_tiles_mode(p, n_tiles, codes, scale_inv, near_mid, rel, 0);
+}
+
 /* [ZeRO-FP8, "Summary"]: the element-wise update of the rank's slice, then
  * the new FP8 weights and scales from the updated FP32 master. */
+void ora_step_mode(float* p, const float* g, float* m, float* v, int64_t n_tiles,
+                   const ora_hparams* hp, uint8_t* codes, float* scale_inv,
+                   uint8_t* near_mid, double rel, int pow2) {
+    ora_adamw(p, g, m, v, n_tiles * ORA_TILE_ELEMS, hp);
+    ora_quant_tiles_mode(p, n_tiles, codes, scale_inv, near_mid, rel, pow2);
+}
+
 void ora_step(float* p, const float* g, float* m, float* v, int64_t n_tiles,
               const ora_hparams* hp, uint8_t* codes, float* scale_inv,
               uint8_t* near_mid, double rel) {
-    ora_adamw(p, g, m, v, n_tiles * ORA_TILE_ELEMS, hp);
-    ora_quant_tiles(p, n_tiles, codes, scale_inv, near_mid, rel);
+    ora_step_mode(p, g, m, v, n_tiles, hp, codes, scale_inv, near_mid, rel, 0);
 }

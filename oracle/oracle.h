@@ -86,21 +86,37 @@ void ora_unpack(const int64_t* dims, int32_t n_params, const uint8_t* codes,
                 const float* scale_inv, const int64_t* table, int64_t q,
                 uint8_t* const* dst_codes, float* const* dst_scale);
 
+/* Transposed copy of power-of-two-quantized tiles: for every owned slot,
+ * W^T[e][128 j + c][128 i + r] = code of the value at (r, c) of the tile,
+ * requantized with one power-of-two scale per 128-element group of a W^T
+ * row (a column segment of the tile).  dst_t[p]: uint8 [E, W, H];
+ * dst_t_scale[p]: float [E, W, ceil(H/128)]. */
+void ora_transpose_pow2(const int64_t* dims, int32_t n_params, const uint8_t* codes,
+                        const float* scale_inv, const int64_t* table, int64_t q,
+                        uint8_t* const* dst_t, float* const* dst_t_scale);
+
 /* ---- AdamW (element-wise, fp32) ----------------------------------- */
 void ora_adamw(float* p, const float* g, float* m, float* v, int64_t n,
                const ora_hparams* hp);
 
 /* ---- Per-tile E4M3 quantization ----------------------------------- */
+/* Smallest power of two 2^T with 448 * 2^T >= amax (amax > 0), T >= -149. */
+float ora_pow2_scale(float amax);
 /* n_tiles tiles of 16384 contiguous values.  near_mid (nullable) gets a 1
  * for every element whose quotient p/scale_inv is within rel of an E4M3
- * rounding midpoint. */
+ * rounding midpoint.  pow2 != 0: power-of-two scales (ora_pow2_scale). */
 void ora_quant_tiles(const float* p, int64_t n_tiles, uint8_t* codes,
                      float* scale_inv, uint8_t* near_mid, double rel);
+void ora_quant_tiles_mode(const float* p, int64_t n_tiles, uint8_t* codes,
+                          float* scale_inv, uint8_t* near_mid, double rel, int pow2);
 
 /* ---- The fused step: AdamW then per-tile requantization ----------- */
 void ora_step(float* p, const float* g, float* m, float* v, int64_t n_tiles,
               const ora_hparams* hp, uint8_t* codes, float* scale_inv,
               uint8_t* near_mid, double rel);
+void ora_step_mode(float* p, const float* g, float* m, float* v, int64_t n_tiles,
+                   const ora_hparams* hp, uint8_t* codes, float* scale_inv,
+                   uint8_t* near_mid, double rel, int pow2);
 
 #ifdef __cplusplus
 }

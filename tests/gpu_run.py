@@ -14,8 +14,8 @@ from synth import workloads as WL
 TILE_ELEMS = bfz.TILE_ELEMS
 
 
-def hp_for(w, t):
-    return bfz.AdamW(step=t, **WL.HP)
+def hp_for(w, t, pow2=False):
+    return bfz.AdamW(step=t, scale_pow2=int(pow2), **WL.HP)
 
 
 class GpuWorkload:
@@ -23,7 +23,7 @@ class GpuWorkload:
 
     MODES = ("unfused", "fused", "fused_unpack")
 
-    def __init__(self, w: WL.Workload, device="cuda", mode="unfused"):
+    def __init__(self, w: WL.Workload, device="cuda", mode="unfused", pow2=False):
         """mode: how a step is taken --
         "unfused": pack_shard + adamw_fp8_step (then unpack_fp8 on demand);
         "fused": fold_adamw_fp8_step (gradients read row-major);
@@ -32,6 +32,7 @@ class GpuWorkload:
         assert mode in self.MODES, mode
         self.w = w
         self.mode = mode
+        self.pow2 = pow2  # power-of-two tile scales
         self.device = torch.device(device)
         with torch.cuda.device(self.device):
             self.plan = bfz.Plan(w.dims, w.D, w.rank)
@@ -84,16 +85,16 @@ class GpuWorkload:
 
     def step(self, t):
         bfz.adamw_fp8_step(self.master, self.grad, self.m, self.v, self.codes, self.scale_inv,
-                           hp_for(self.w, t))
+                           hp_for(self.w, t, self.pow2))
 
     def fold_step(self, t):
         bfz.fold_adamw_fp8_step(self.plan, self.grad_rm, self.master, self.m, self.v, self.codes,
-                                self.scale_inv, hp_for(self.w, t))
+                                self.scale_inv, hp_for(self.w, t, self.pow2))
 
     def fold_step_unpack(self, t):
         bfz.fold_adamw_fp8_step_unpack(self.plan, self.grad_rm, self.master, self.m, self.v,
                                        self.codes, self.scale_inv, self.out_fp8, self.out_scale,
-                                       hp_for(self.w, t))
+                                       hp_for(self.w, t, self.pow2))
 
     def apply(self, t):
         """One step on the current row-major gradients."""

@@ -19,7 +19,7 @@ def _fold_rect(w, tensor, p, e, i, j, vr, vc, step=0):
     return oracle.fold_tile(np.ascontiguousarray(rect.reshape(1, vr, vc)), 0, 0, 0)
 
 
-def oracle_slot(w, row, steps=None, rel=1e-6):
+def oracle_slot(w, row, steps=None, rel=1e-6, pow2=False):
     """Final master/m/v tile, codes, scale_inv and midpoint flags of the slot
     whose oracle plan row is `row` = (p, e, i, j, vr, vc)."""
     p, e, i, j, vr, vc = (int(x) for x in row)
@@ -35,16 +35,16 @@ def oracle_slot(w, row, steps=None, rel=1e-6):
     out = None
     for t in (steps or w.steps):
         codes, scale, near = oracle.step(master, grads[t], m, v,
-                                         oracle.hparams(step=t, **WL.HP), rel)
+                                         oracle.hparams(step=t, **WL.HP), rel, pow2)
         out = (codes, scale, near)
     return dict(master=master, m=m, v=v, codes=out[0], scale_inv=out[1][0], near=out[2])
 
 
-def oracle_slots(w, slots, steps=None, rel=1e-6, threads=None):
+def oracle_slots(w, slots, steps=None, rel=1e-6, threads=None, pow2=False):
     q, owned, table = oracle.plan(w.dims, w.D, w.rank)
     threads = threads or min(16, os.cpu_count() or 4)
     with ThreadPoolExecutor(max_workers=threads) as ex:
-        res = list(ex.map(lambda s: oracle_slot(w, table[s], steps, rel), slots))
+        res = list(ex.map(lambda s: oracle_slot(w, table[s], steps, rel, pow2), slots))
     keys = ("master", "m", "v", "codes", "near")
     out = {k: np.stack([r[k] for r in res]) for k in keys}
     out["scale_inv"] = np.array([r["scale_inv"] for r in res], dtype=np.float32)

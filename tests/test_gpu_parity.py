@@ -211,7 +211,9 @@ def test_random_configurations(seed):
               beta2=float(rng.choice([0.9, 0.95, 0.999])), eps=float(10 ** rng.uniform(-10, -3)),
               weight_decay=float(rng.choice([0.0, 0.01, 0.3])))
     t = int(rng.choice([1, 2, 57, 10 ** 6]))
-    _say("random config seed", 1000 + seed, "dims", dims, "D", D, "rank", rank, "hp", hp, "t", t)
+    pow2 = bool(seed % 2)
+    _say("random config seed", 1000 + seed, "dims", dims, "D", D, "rank", rank, "hp", hp, "t", t,
+         "pow2 scales", pow2)
     q, owned, table = oracle.plan(dims, D, rank)
     scale = float(10 ** rng.uniform(-4, 1))
     host = {k: [rng.normal(0, s, d).astype(np.float32) for d in dims]
@@ -219,7 +221,7 @@ def test_random_configurations(seed):
     host["v"] = [np.square(rng.normal(0, scale * 1e-2, d)).astype(np.float32) for d in dims]
     ora_state = {k: oracle.pack(dims, host[k], table) for k in ("p", "g", "m", "v")}
     codes_o, scale_o, near_o = oracle.step(ora_state["p"], ora_state["g"], ora_state["m"],
-                                           ora_state["v"], oracle.hparams(step=t, **hp))
+                                           ora_state["v"], oracle.hparams(step=t, **hp), pow2=pow2)
     plan = bfz.Plan(dims, D, rank)
     dev = {k: [torch.from_numpy(x.reshape(-1)).cuda() for x in host[k]] for k in host}
     for route in ("unfused", "fused", "fused_unpack"):
@@ -229,7 +231,7 @@ def test_random_configurations(seed):
             bfz.pack_shard(plan, dev[k], st[k])
         codes = torch.empty(q * 16384, dtype=torch.uint8, device="cuda")
         sc = torch.empty(q, dtype=torch.float32, device="cuda")
-        h = bfz.AdamW(step=t, **hp)
+        h = bfz.AdamW(step=t, scale_pow2=int(pow2), **hp)
         if route == "unfused":
             gt = torch.empty(q * 16384, dtype=torch.float32, device="cuda")
             bfz.pack_shard(plan, dev["g"], gt)

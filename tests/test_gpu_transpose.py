@@ -1,0 +1,97 @@
+"""GPU parity of the power-of-two step and of the exponent-edit transpose
+(bfz_transpose_pow2) against the oracle (needs an MI355X).  Byte results
+must be bit-exact."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import blockwise_fp8_zero_amd as bfz
+import oracle
+from synth import workloads as WL
+from tests.compare import compare
+from tests.gpu_run import GpuWorkload
+from tests.oracle_run import oracle_slots
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[gpu-transpose]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _outputs(dims, device):
+    dt = [torch.full((E * W * H,), 0xAA, dtype=torch.uint8, device=device) for E, H, W in dims]
+    ds = [torch.full((E * W * -(-H // 128),), -1.0, dtype=torch.float32, device=device)
+          for E, H, W in dims]
+    return dt, ds
+
+
+def _oracle_outputs(dims):
+    dt = [np.full((E, W, H), 0xAA, dtype=np.uint8) for E, H, W in dims]
+    ds = [np.full((E, W, -(-H // 128)), -1.0, dtype=np.float32) for E, H, W in dims]
+    return dt, ds
+
+
+CASES = [
+    ([(1, 256, 384)], 1, 0),
+    ([(2, 300, 129), (1, 77, 513), (1, 1, 1)], 1, 0),
+    ([(3, 129, 130), (1, 128, 1000)], 3, 1),
+    ([(1, 640, 48)] * 70, 2, 1),   # > 64 weights: several launch segments
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_transpose_random_codes(case):
+    """Random codes (NaN patterns excluded) on random power-of-two scales,
+    including the 2^-149 floor, with zero columns mixed in."""
+    dims, D, rank = CASES[case]
+    _say("random codes case", case, "D", D, "rank", rank, "weights", len(dims))
+    rng = np.random.default_rng(40 + case)
+    q, owned, table = oracle.plan(dims, D, rank)
+    codes = rng.integers(0, 256, q * 16384).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x7E
+    codes.reshape(q, 128, 128)[:, :, ::7] = 0              # all-zero columns
+    codes.reshape(q, 128, 128)[:, :, 3::11] &= 0x87        # small magnitudes, subnormals
+    T = rng.integers(-149, 100, q)
+    T[: min(q, 3)] = [-149, -145, -140][: min(q, 3)]
+    scale = np.ldexp(1.0, T).astype(np.float32)
+    odt, ods = _oracle_outputs(dims)
+    oracle.transpose_pow2(dims, codes, scale, table, odt, ods)
+    plan = bfz.Plan(dims, D, rank)
+    dt, ds = _outputs(dims, "cuda")
+    bfz.transpose_pow2(plan, torch.from_numpy(codes).cuda(), torch.from_numpy(scale).cuda(), dt, ds)
+    torch.cuda.synchronize()
+    for p in range(len(dims)):
+        assert np.array_equal(dt[p].cpu().numpy(), odt[p].reshape(-1)), p
+        assert np.array_equal(ds[p].cpu().numpy(), ods[p].reshape(-1)), p
+
+
+@pytest.mark.parametrize("mode", GpuWorkload.MODES)
+def test_pow2_step_then_transpose(mode):
+    """The flow: a power-of-two step of the ragged workload (every slot vs
+    the oracle), then the transposed copy of its codes."""
+    w = WL.ragged()
+    w.dims = w.dims[:10]
+    _say("pow2 step + transpose: 10 ragged matrices, D=8 rank 3, mode", mode)
+    g = GpuWorkload(w, mode=mode, pow2=True)
+    g.load_state()
+    g.run_steps()
+    slots = list(range(g.q))
+    ora = oracle_slots(w, slots, pow2=True)
+    rep = compare(g.tiles(slots), ora)
+    _say({k: v for k, v in rep.items() if k != "fail"})
+    assert rep["ok"] and rep["exact"], rep["fail"]
+    sc = ora["scale_inv"]
+    assert (np.frexp(sc)[0] == 0.5).all()
+    q, owned, table = oracle.plan(w.dims, w.D, w.rank)
+    odt, ods = _oracle_outputs(w.dims)
+    oracle.transpose_pow2(w.dims, ora["codes"].reshape(-1), sc, table, odt, ods)
+    dt, ds = _outputs(w.dims, "cuda")
+    bfz.transpose_pow2(g.plan, g.codes, g.scale_inv, dt, ds)
+    torch.cuda.synchronize()
+    for p in g.touched:
+        assert np.array_equal(dt[p].cpu().numpy(), odt[p].reshape(-1)), p
+        assert np.array_equal(ds[p].cpu().numpy(), ods[p].reshape(-1)), p

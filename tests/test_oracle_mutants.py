@@ -20,6 +20,7 @@ from tests import test_oracle_e4m3 as E
 from tests import test_oracle_layout as L
 from tests import test_oracle_plan as P
 from tests import test_oracle_quant as Q
+from tests import test_oracle_transpose as X
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -37,7 +38,7 @@ MUTANTS = {
     "ties round up": ("c = (k % 2 == 0) ? k : k + 1;", "c = k + 1;"),
     "saturates at the FNUZ maximum": ("if (a > 448.0) a = 448.0;", "if (a > 240.0) a = 240.0;"),
     "sign bit dropped": ("signbit(y) ? (c | 0x80) : c", "c"),
-    "scale uses 240": ("float s = amax / 448.0f;", "float s = amax / 240.0f;"),
+    "scale uses 240": (": amax / 448.0f;", ": amax / 240.0f;"),
     "quotient multiplies by the scale": ("float y = x[k] / s;", "float y = x[k] * s;"),
     "zero tile scale 0": ("scale_inv[t] = 1.0f;", "scale_inv[t] = 0.0f;"),
     "amax ignores negatives": ("if (fabsf(x[k]) > amax) amax = fabsf(x[k]);", "if (x[k] > amax) amax = x[k];"),
@@ -46,6 +47,12 @@ MUTANTS = {
                                           "if (pick < 0 || size < pick_size) { pick = p; pick_size = size; }"),
     "param-wise: fullest bucket": ("if (bucket_elems[b] < bucket_elems[best]) best = b;",
                                    "if (bucket_elems[b] > bucket_elems[best]) best = b;"),
+    "power-of-two scale rounds down": ("while (ldexp(448.0, T) < (double)amax) ++T;",
+                                       "while (ldexp(448.0, T + 1) < (double)amax) ++T;"),
+    "transpose: group scale one step too small": ("while (ldexp(448.0, T) < amax) ++T;",
+                                                  "while (ldexp(448.0, T + 1) < amax) ++T;"),
+    "transpose: W^T row stride W": ("dst_t[p][out_row * H + ORA_TILE_DIM * i + r] = code;",
+                                    "dst_t[p][out_row * W + ORA_TILE_DIM * i + r] = code;"),
     "valid rows from W": ("row[4] = (H - ORA_TILE_DIM * i) < ORA_TILE_DIM ? H - ORA_TILE_DIM * i : ORA_TILE_DIM;",
                           "row[4] = (W - ORA_TILE_DIM * i) < ORA_TILE_DIM ? W - ORA_TILE_DIM * i : ORA_TILE_DIM;"),
     "fold transposes the tile": ("tile[a * ORA_TILE_DIM + b] =", "tile[b * ORA_TILE_DIM + a] ="),
@@ -73,7 +80,9 @@ def _pins():
         pins.append(lambda kind=kind: Q.test_invariants(o, kind))
         pins.append(lambda kind=kind: Q.test_same_layout_requant_is_idempotent(o, kind))
     pins += [lambda: Q.test_exact_grid_tile(o), lambda: Q.test_block_quantize_multiply_form(o),
-             lambda: Q.test_zero_tile_guard_and_padding(o)]
+             lambda: Q.test_zero_tile_guard_and_padding(o), lambda: Q.test_pow2_scale_edges(o)]
+    for kind in ("normal", "heavy", "wide"):
+        pins.append(lambda kind=kind: Q.test_pow2_invariants(o, kind))
     pins += [lambda s=s: P.test_brute_force_ownership(o, s) for s in range(4)]
     pins += [lambda: P.test_toy_walkthrough(o), lambda: P.test_workload_counts(o),
              lambda: P.test_more_ranks_than_tiles(o), lambda: P.test_paramwise_graham_worst_case(o),
@@ -82,6 +91,9 @@ def _pins():
     pins += [lambda sh=sh: L.test_pack_matches_im2col(o, sh) for sh in L.SHAPES]
     pins += [lambda sh=sh: L.test_unpack_matches_col2im(o, sh) for sh in L.SHAPES]
     pins.append(lambda: L.test_round_trip_multi_param_multi_rank(o))
+    for case in range(len(X.SHAPES)):
+        pins.append(lambda case=case: X.test_transpose_is_lossless(o, case))
+        pins.append(lambda case=case: X.test_transpose_matches_torch_route(o, case))
     return pins
 
 

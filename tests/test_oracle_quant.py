@@ -123,3 +123,54 @@ def test_zero_tile_guard_and_padding(ora):
     assert scale[0] == 1.0 and (codes[:T] == 0).all()
     assert scale[1] == np.float32(np.float32(1e-30) / np.float32(448.0))
     assert codes[T + 5] == 0x7E and (np.delete(codes[T:], 5) == 0).all()
+
+
+# ---- power-of-two scales ------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["normal", "heavy", "wide"])
+def test_pow2_invariants(ora, kind):
+    """Power-of-two tile scales ("FP8-Flow-MoE" §3.1): the scale is 2^T,
+    the smallest power of two with 448 * 2^T >= amax, so the largest code
+    decodes into [224, 448]; every quotient x / 2^T is exact, so the codes
+    equal torch's E4M3 cast of the exactly scaled values."""
+    dec = _decode_all(ora)
+    p = _tiles(4, 6, kind)
+    p[5 * T:] = 0.0
+    codes, scale, _ = ora.quant_tiles(p, pow2=True)
+    for t in range(6):
+        x = p[t * T:(t + 1) * T].astype(np.float64)
+        c = codes[t * T:(t + 1) * T]
+        s = float(scale[t])
+        if t == 5:
+            assert s == 1.0 and (c == 0).all()
+            continue
+        m, e = np.frexp(s)
+        assert m == 0.5  # a power of two
+        amax = np.abs(x).max()
+        assert 448 * s >= amax and (448 * s / 2 < amax or s == 2.0 ** -149)
+        top = np.abs(dec[c]).max()
+        assert 224 <= top <= 448
+        y = torch.from_numpy((x / s).astype(np.float32))  # exact: s is a power of two
+        ref = y.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(ref, c)
+
+
+@pytest.mark.parametrize("kind", ["normal", "wide"])
+def test_pow2_requant_is_exactly_idempotent(ora, kind):
+    dec = _decode_all(ora)
+    p = _tiles(5, 4, kind)
+    codes, scale, _ = ora.quant_tiles(p, pow2=True)
+    deq = (dec[codes] * np.repeat(scale.astype(np.float64), T)).astype(np.float32)
+    assert np.array_equal(deq.astype(np.float64), dec[codes] * np.repeat(scale.astype(np.float64), T))
+    codes2, scale2, _ = ora.quant_tiles(deq, pow2=True)
+    assert np.array_equal(scale2, scale) and np.array_equal(codes2, codes)
+
+
+def test_pow2_scale_edges(ora):
+    assert ora.pow2_scale(448.0) == 1.0
+    assert ora.pow2_scale(448.0001) == 2.0
+    assert ora.pow2_scale(224.0) == 0.5
+    assert ora.pow2_scale(224.0001) == 1.0
+    assert ora.pow2_scale(448.0 * 2.0 ** -20) == 2.0 ** -20
+    assert ora.pow2_scale(2.0 ** -149) == 2.0 ** -149  # the clamp
+    assert ora.pow2_scale(3.0e38) == 2.0 ** 120
