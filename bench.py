@@ -46,7 +46,8 @@ PACK_BYTES_PER_ELEM = 8           # read grad + write tile
 UNPACK_BYTES_PER_ELEM = 2         # read code + write code
 UNPACK_BYTES_PER_TILE = 8         # read + write scale
 TRAFFIC_FILES = {k: os.path.join(ROOT, "profiles", f"{k}_dense_llm_traffic.md")
-                 for k in ("fold_step_unfold_kernel", "fold_step_kernel", "step_kernel")}
+                 for k in ("fold_step_unfold_kernel", "fold_step_kernel", "step_kernel",
+                           "transpose_pow2_kernel")}
 KERNEL_OF_PATH = {"fused_unpack": "fold_step_unfold_kernel", "fused": "fold_step_kernel",
                   "unfused": "step_kernel"}
 KERNEL_SRC = os.path.join(ROOT, "blockwise_fp8_zero_amd", "csrc", "kernels.hip")
@@ -73,6 +74,17 @@ def measured_traffic(kernel):
     if not sha or not tb or sha.group(1) != kernel_sha():
         return None
     return float(tb.group(1))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(w, target_s=10.0):
@@ -119,24 +131,36 @@ def cpu_baseline(w, target_s=10.0):
                 np.empty(n, np.uint8), np.empty(q, np.float32), np.empty(E * H * W, np.uint8),
                 np.empty(q, np.float32)]
 
-    # calibrate the number of passes on one thread
+    # calibrate the number of passes on one thread (the second pass: the
+    # first one takes the page faults of the fresh buffers)
     st = new_state()
+    one_pass(st)
     t0 = time.perf_counter()
     one_pass(st)
     per_pass = time.perf_counter() - t0
     passes = max(1, int(round(target_s / per_pass)))
+    # a one-thread figure on the same slab, about a tenth of the threaded time
+    passes1 = max(1, int(round(0.1 * target_s / per_pass)))
+    t0 = time.perf_counter()
+    for _ in range(passes1):
+        one_pass(st)
+    one_thread = passes1 * n / (time.perf_counter() - t0)
     states = [new_state() for _ in range(threads)]
 
-    def work(k):
-        for _ in range(passes):
+    def work(k, count):
+        for _ in range(count):
             one_pass(states[k])
 
-    t0 = time.perf_counter()
     with ThreadPoolExecutor(max_workers=threads) as ex:
-        list(ex.map(work, range(threads)))
-    dt = time.perf_counter() - t0
+        # one untimed pass per thread first: it takes the page faults of the
+        # freshly allocated buffers, which serialize across threads
+        list(ex.map(lambda k: work(k, 1), range(threads)))
+        t0 = time.perf_counter()
+        list(ex.map(lambda k: work(k, passes), range(threads)))
+        dt = time.perf_counter() - t0
     elems = threads * passes * n
     return {"value": elems / dt, "unit": "elem/s", "cores": threads, "kind": "oracle",
+            "one_thread_value": one_thread, "nproc": os.cpu_count(), "cpu_model": cpu_model(),
             "sample": f"fold + AdamW/E4M3 step + unfold of a {H}x{W} slab (256 tiles, "
                       f"{n / 1e6:.1f}M elements) of the first dense-LLM weight at t="
                       f"{w.measured_step}, {passes} passes on each of {threads} threads, "
@@ -178,8 +202,10 @@ def time_transpose(g, t, steps, stream):
     # scale per valid column of every owned tile
     algo = g.q * bfz.TILE_ELEMS + 4 * g.q + valid + 4 * int(owned[:, 5].sum())
     del dt, ds
+    traffic = measured_traffic("transpose_pow2_kernel") if g.w.name == "dense_llm" else None
     return {"kernel": "transpose_pow2_kernel", "ms": ms, "algorithmic_bytes": algo,
-            "GBps": algo / (ms * 1e-3) / 1e9, "frac": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+            "GBps": algo / (ms * 1e-3) / 1e9, "frac": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "traffic": traffic}
 
 
 def main():

@@ -401,41 +401,64 @@ __device__ __forceinline__ float pow2_value(int T) {
     return T >= -126 ? __uint_as_float((uint32_t)(T + 127) << 23) : __uint_as_float(1u << (T + 149));
 }
 
+// Largest E4M3 magnitude (low 7 bits) among the 16 codes of four words.
+__device__ __forceinline__ uint32_t mag_max16(const uint32_t v[4]) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t a = max(__builtin_amdgcn_ubfe(v[q], 0, 7), __builtin_amdgcn_ubfe(v[q], 8, 7));
+        const uint32_t b = max(__builtin_amdgcn_ubfe(v[q], 16, 7), __builtin_amdgcn_ubfe(v[q], 24, 7));
+        m = max(m, max(a, b));
+    }
+    return m;
+}
+
 // One 256-thread workgroup per owned slot.
-//  1. Thread t reads 4x4-byte blocks of the tile (block column t % 32, block
-//     rows t / 32 + 8 m), transposes each in registers and writes its four
-//     columns to LDS as words of W^T rows: W^T row c (= tile column c) holds
-//     bytes r = 0..127 (= tile rows).  Word w of row c sits at c * 32 +
-//     ((w + c / 4) % 32), a rotation that spreads a wave's writes over all
-//     32 banks.
-//  2. Eight consecutive lanes own one W^T row, 16 bytes each, so a wave
-//     stores eight contiguous 128-byte row segments.  The group's largest
-//     magnitude code (valid rows only) is an 8-lane shuffle reduction; it
-//     gives the headroom d (clamped so 2^(T - d) >= 2^-149), every code is
-//     moved up d binades, and lane 0 of the row writes the group scale.
+//  1. Thread t reads rows 4(t / 8) .. +3, bytes 16(t % 8) .. +15 of the tile
+//     (four 16-byte loads), transposes each 4x4-byte block with byte
+//     permutes and writes the 16 resulting words to LDS as words of W^T
+//     rows: W^T row c (= tile column c) holds bytes r = 0..127 (= tile rows)
+//     in 32 words.  Word w of row c sits at c * 32 + ((w + 4 (c / 16)) % 32):
+//     the rotation keeps each aligned group of four words together and puts
+//     exactly two lanes of a wave on every bank in step 1.
+//  2. Eight consecutive lanes own one W^T row, 16 bytes (one aligned 16-byte
+//     LDS read) each, so a wave stores eight contiguous 128-byte row
+//     segments.  The group's largest magnitude code (valid rows only) is an
+//     8-lane shuffle reduction; it gives the headroom d (clamped so
+//     2^(T - d) >= 2^-149), every code is moved up d binades, and lane 0 of
+//     the row writes the group scale.  When a lane's 16 codes are all normal
+//     or zero, the move is one add per word: 8d on the exponent field of each
+//     normal byte (d never carries out of a byte: the headroom keeps every
+//     code <= 126); codes with a subnormal, and ragged edges, go byte by byte.
 // An all-zero column: scale 1, codes 0.
 __global__ __launch_bounds__(kThreads) void transpose_pow2_kernel(
     const TileEntry* __restrict__ entries, const uint8_t* __restrict__ codes,
     const float* __restrict__ scale_inv, TransposeArgs args) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     __shared__ uint32_t tile_t[kTileDim * 32];
     const int64_t slot = blockIdx.x;
     const TileEntry t = entries[slot];
     if (t.local < 0) return;
-    const uint32_t* in = reinterpret_cast<const uint32_t*>(codes + slot * kTileElems);
-    const int bc = threadIdx.x & 31;
+    {
+        const u32x4* in = reinterpret_cast<const u32x4*>(codes + slot * kTileElems);
+        const int cx = threadIdx.x & 7, rq = threadIdx.x >> 3;
+        u32x4 w[4];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-        const int br = (threadIdx.x >> 5) + 8 * mb;
-        uint32_t w[4];
+        for (int k = 0; k < 4; ++k) w[k] = __builtin_nontemporal_load(in + (4 * rq + k) * 8 + cx);
+        const int rot = (rq + 4 * cx) & 31;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) w[k] = in[(4 * br + k) * 32 + bc];
+        for (int wq = 0; wq < 4; ++wq) {
+            // rows 0, 1 (and 2, 3) interleaved byte by byte, then the columns
+            const uint32_t x01lo = __builtin_amdgcn_perm(w[1][wq], w[0][wq], 0x05010400u);
+            const uint32_t x01hi = __builtin_amdgcn_perm(w[1][wq], w[0][wq], 0x07030602u);
+            const uint32_t x23lo = __builtin_amdgcn_perm(w[3][wq], w[2][wq], 0x05010400u);
+            const uint32_t x23hi = __builtin_amdgcn_perm(w[3][wq], w[2][wq], 0x07030602u);
+            const uint32_t col[4] = {__builtin_amdgcn_perm(x23lo, x01lo, 0x05040100u),
+                                     __builtin_amdgcn_perm(x23lo, x01lo, 0x07060302u),
+                                     __builtin_amdgcn_perm(x23hi, x01hi, 0x05040100u),
+                                     __builtin_amdgcn_perm(x23hi, x01hi, 0x07060302u)};
 #pragma unroll
-        for (int l = 0; l < 4; ++l) {
-            const uint32_t col = ((w[0] >> (8 * l)) & 0xFFu) | (((w[1] >> (8 * l)) & 0xFFu) << 8) |
-                                 (((w[2] >> (8 * l)) & 0xFFu) << 16) |
-                                 (((w[3] >> (8 * l)) & 0xFFu) << 24);
-            const int c = 4 * bc + l;
-            tile_t[c * 32 + ((br + bc) & 31)] = col;  // rotation: (br + c / 4) % 32
+            for (int l = 0; l < 4; ++l) tile_t[(16 * cx + 4 * wq + l) * 32 + rot] = col[l];
         }
     }
     __syncthreads();
@@ -447,18 +470,18 @@ __global__ __launch_bounds__(kThreads) void transpose_pow2_kernel(
     const int64_t i = ei % hb, e = ei / hb;
     const int k2 = threadIdx.x & 7;        // 16-byte chunk of the row: rows 16 k2 .. +15
     const int r0 = 16 * k2;
+    const int nvalid = max(0, min(16, (int)t.valid_rows - r0));
 #pragma unroll
     for (int mr = 0; mr < 4; ++mr) {
         const int c = (threadIdx.x >> 3) + 32 * mr;  // W^T row within the tile
-        uint32_t v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = tile_t[c * 32 + ((4 * k2 + q + c / 4) & 31)];
-        // valid rows of this chunk, then the row's largest magnitude code
-        const int nvalid = max(0, min(16, (int)t.valid_rows - r0));
+        const u32x4 vv = *reinterpret_cast<const u32x4*>(&tile_t[c * 32 + ((4 * k2 + 4 * (c >> 4)) & 31)]);
+        const uint32_t v[4] = {vv[0], vv[1], vv[2], vv[3]};
         uint32_t mx = 0;
-#pragma unroll
-        for (int l = 0; l < 16; ++l)
-            if (l < nvalid) mx = max(mx, (v[l >> 2] >> (8 * (l & 3))) & 0x7Fu);
+        if (nvalid == 16) {
+            mx = mag_max16(v);
+        } else {
+            for (int l = 0; l < nvalid; ++l) mx = max(mx, (v[l >> 2] >> (8 * (l & 3))) & 0x7Fu);
+        }
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1, 64));
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2, 64));
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 4, 64));
@@ -470,14 +493,27 @@ __global__ __launch_bounds__(kThreads) void transpose_pow2_kernel(
         if (nvalid == 0) continue;
         uint32_t o[4] = {0u, 0u, 0u, 0u};
         if (mx != 0u) {
+            // per byte: bit 7 of nf set for a normal code (exponent field != 0);
+            // sub collects nonzero codes that are not normal
+            uint32_t nf[4], sub = 0;
 #pragma unroll
-            for (int l = 0; l < 16; ++l)
-                o[l >> 2] |= (l < nvalid ? e4m3_scale_up((v[l >> 2] >> (8 * (l & 3))) & 0xFFu, d) : 0u)
-                             << (8 * (l & 3));
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t a = v[q] & 0x7F7F7F7Fu;
+                nf[q] = ((a & 0x78787878u) + 0x78787878u) & 0x80808080u;
+                sub |= ((a + 0x7F7F7F7Fu) & 0x80808080u) & ~nf[q];
+            }
+            if (nvalid == 16 && sub == 0u) {
+                const uint32_t inc = (uint32_t)d << 3;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) o[q] = v[q] + (nf[q] >> 7) * inc;
+            } else {
+                for (int l = 0; l < 16; ++l)
+                    o[l >> 2] |= (l < nvalid ? e4m3_scale_up((v[l >> 2] >> (8 * (l & 3))) & 0xFFu, d) : 0u)
+                                 << (8 * (l & 3));
+            }
         }
         uint8_t* q = args.codes[t.local] + out_row * H + kTileDim * i + r0;
         if (nvalid == 16 && (reinterpret_cast<uintptr_t>(q) & 15u) == 0) {
-            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
             const u32x4 y = {o[0], o[1], o[2], o[3]};
             __builtin_nontemporal_store(y, reinterpret_cast<u32x4*>(q));
         } else {

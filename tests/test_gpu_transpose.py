@@ -95,3 +95,34 @@ def test_pow2_step_then_transpose(mode):
     for p in g.touched:
         assert np.array_equal(dt[p].cpu().numpy(), odt[p].reshape(-1)), p
         assert np.array_equal(ds[p].cpu().numpy(), ods[p].reshape(-1)), p
+
+
+def test_transpose_quantized_weights():
+    """Codes of power-of-two-quantized Gaussian weights on full, 16-byte
+    aligned tiles -- mostly normal codes, where whole words are moved at
+    once -- with a sprinkling of values small enough to give subnormal
+    codes, and zero columns, so both routes meet inside one wave."""
+    dims = [(2, 512, 384), (1, 1024, 640), (1, 256, 4096)]
+    _say("quantized Gaussian weights", dims)
+    rng = np.random.default_rng(77)
+    ws = []
+    for E, H, W in dims:
+        x = rng.normal(0, 1, (E, H, W)) * 10.0 ** rng.uniform(-1, 0.5, (E, 1, W))
+        amax = np.abs(x).max()
+        tiny = rng.random((E, H, W)) < 2e-4
+        x[tiny] = amax * 2.0 ** -13 * np.sign(rng.normal(size=int(tiny.sum())))
+        x[:, :, ::37] = 0.0
+        ws.append(x.astype(np.float32))
+    q, owned, table = oracle.plan(dims, 1, 0)
+    codes, scale, _ = oracle.quant_tiles(oracle.pack(dims, ws, table), pow2=True)
+    mags = codes & 0x7F
+    assert ((mags > 0) & (mags < 8)).sum() > 100 and (mags >= 8).mean() > 0.5
+    odt, ods = _oracle_outputs(dims)
+    oracle.transpose_pow2(dims, codes, scale, table, odt, ods)
+    plan = bfz.Plan(dims, 1, 0)
+    dt, ds = _outputs(dims, "cuda")
+    bfz.transpose_pow2(plan, torch.from_numpy(codes).cuda(), torch.from_numpy(scale).cuda(), dt, ds)
+    torch.cuda.synchronize()
+    for p in range(len(dims)):
+        assert np.array_equal(dt[p].cpu().numpy(), odt[p].reshape(-1)), p
+        assert np.array_equal(ds[p].cpu().numpy(), ods[p].reshape(-1)), p
