@@ -144,12 +144,42 @@ struct RowMajorGrad {
     __device__ __forceinline__ f32x4 operator()(int k) const {
         const int r = k * 32 + (threadIdx.x >> 5), c = 4 * (threadIdx.x & 31);
         f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (origin == nullptr || r >= rows) return x;
-        const float* q = origin + (int64_t)r * ld + c;
-        if (vec && c + 4 <= cols) return load_stream(reinterpret_cast<const f32x4*>(q));
+        if (origin == nullptr) return x;
+        if (vec) {
+            if (r >= rows) return x;
+            const float* q = origin + (int64_t)r * ld + c;
+            if (c + 4 <= cols) return load_stream(reinterpret_cast<const f32x4*>(q));
+#pragma unroll
+            for (int l = 0; l < 4; ++l)
+                if (c + l < cols) x[l] = q[l];
+            return x;
+        }
+        // A row that starts a floats past a 16-byte boundary: lane l loads the
+        // aligned block holding row elements c - a .. c - a + 3 and takes the
+        // a elements it lacks from its right neighbour's block (the row's last
+        // lane loads one more block).  A block is read only if it holds an
+        // element of the row's valid part; an aligned 16-byte block never
+        // crosses a page, so every read stays in mapped memory.  Both rows of
+        // a wave run the shuffle unconditionally (32-lane segments).
+        const bool row_ok = r < rows;
+        const float* row = origin + (int64_t)(row_ok ? r : 0) * ld;
+        const int a = (int)((reinterpret_cast<uintptr_t>(row) >> 2) & 3u);
+        const f32x4* blk = reinterpret_cast<const f32x4*>(row - a) + (c >> 2);
+        const bool last = (threadIdx.x & 31) == 31;
+        f32x4 f = {0.0f, 0.0f, 0.0f, 0.0f}, g = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (row_ok && c - a < cols) f = load_stream(blk);
+        if (row_ok && last && a > 0 && kTileDim - a < cols) g = load_stream(blk + 1);
+        f32x4 n;
+#pragma unroll
+        for (int l = 0; l < 4; ++l) n[l] = __shfl_down(f[l], 1, 32);
+        if (last) n = g;
+        x[0] = a == 0 ? f[0] : a == 1 ? f[1] : a == 2 ? f[2] : f[3];
+        x[1] = a == 0 ? f[1] : a == 1 ? f[2] : a == 2 ? f[3] : n[0];
+        x[2] = a == 0 ? f[2] : a == 1 ? f[3] : a == 2 ? n[0] : n[1];
+        x[3] = a == 0 ? f[3] : a == 1 ? n[0] : a == 2 ? n[1] : n[2];
 #pragma unroll
         for (int l = 0; l < 4; ++l)
-            if (c + l < cols) x[l] = q[l];
+            if (!row_ok || c + l >= cols) x[l] = 0.0f;
         return x;
     }
 };

@@ -49,6 +49,30 @@ def test_pack_matches_oracle(case):
     assert np.array_equal(dst.cpu().numpy().view(np.uint32), want.view(np.uint32))
 
 
+@pytest.mark.parametrize("off", [0, 1, 2, 3])
+def test_pack_offset_bases(off):
+    """Weights that start `off` floats past a 16-byte boundary: every row
+    misalignment 0..3 meets widths that are and are not multiples of 4,
+    right-edge tiles and single-row tiles."""
+    dims = [(1, 129, 300), (2, 200, 257), (1, 77, 128), (1, 130, 131), (1, 1, 515)]
+    _say("pack with weights offset by", off, "floats")
+    rng = np.random.default_rng(100 + off)
+    hosts = [rng.normal(0, 1, d).astype(np.float32) for d in dims]
+    q, owned, table = oracle.plan(dims, 1, 0)
+    want = oracle.pack(dims, hosts, table)
+    plan = bfz.Plan(dims, 1, 0)
+    devs = []
+    for h in hosts:
+        raw = torch.full((h.size + 8,), float("nan"), dtype=torch.float32, device="cuda")
+        raw[off:off + h.size] = torch.from_numpy(h.reshape(-1)).cuda()
+        devs.append(raw[off:off + h.size])
+    assert all(d.data_ptr() % 16 == 4 * off for d in devs)
+    dst = torch.full((q * 16384,), float("nan"), dtype=torch.float32, device="cuda")
+    bfz.pack_shard(plan, devs, dst)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
 @pytest.mark.parametrize("case", range(len(CASES)))
 def test_unpack_matches_oracle(case):
     dims, D, rank = CASES[case]

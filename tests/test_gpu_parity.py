@@ -309,13 +309,16 @@ def test_deterministic_and_empty():
     assert torch.equal(before, g.codes)
 
 
-def test_fused_routes_equal_unfused_on_misaligned_buffers():
-    """Gradients that start 4 bytes into their buffer (no 16-byte vector
-    path) and FP8 destinations that start 1 byte in (no 32-bit stores) give
-    the same bits through all three routes, and without the tile-major copy."""
-    dims = [(1, 300, 260), (2, 129, 516), (1, 128, 128)]
-    _say("fused vs pack+step, misaligned gradients, seed 21")
-    rng = np.random.default_rng(21)
+@pytest.mark.parametrize("off", [1, 2, 3])
+def test_fused_routes_equal_unfused_on_misaligned_buffers(off):
+    """Gradients that start `off` floats into their buffer (no 16-byte
+    vector path) and FP8 destinations that start 1 byte in (no 32-bit
+    stores) give the same bits through all routes, and without the
+    tile-major copy.  The reference route steps the oracle's fold of the
+    gradients, so it shares no row-major loader with the routes checked."""
+    dims = [(1, 300, 260), (2, 129, 516), (1, 128, 128), (1, 131, 387)]
+    _say("fused vs oracle fold + step, gradients offset by", off, "floats, seed", 20 + off)
+    rng = np.random.default_rng(20 + off)
     plan = bfz.Plan(dims, 2, 1)
     q = plan.shard_tiles
     n = q * 16384
@@ -324,10 +327,15 @@ def test_fused_routes_equal_unfused_on_misaligned_buffers():
     for x in state0:  # padding slots hold zero state
         x.view(q, 16384)[plan.owned_tiles:] = 0
     state0[2].abs_()
-    grads = []
+    grads, host_grads = [], []
     for d in dims:
-        raw = torch.from_numpy(rng.normal(0, 1e-3, int(np.prod(d)) + 1).astype(np.float32)).cuda()
-        grads.append(raw[1:])
+        h = rng.normal(0, 1e-3, d).astype(np.float32)
+        raw = torch.zeros(h.size + 4, dtype=torch.float32, device="cuda")
+        raw[off:off + h.size] = torch.from_numpy(h.reshape(-1)).cuda()
+        grads.append(raw[off:off + h.size])
+        host_grads.append(h)
+    _, _, table = oracle.plan(dims, 2, 1)
+    folded = torch.from_numpy(oracle.pack(dims, host_grads, table)).cuda()
     hb = [(d[0], -(-d[1] // 128), -(-d[2] // 128)) for d in dims]
     outs = []
     for route in ("unfused", "fused", "fused_unpack", "rowmajor_only"):
@@ -339,9 +347,7 @@ def test_fused_routes_equal_unfused_on_misaligned_buffers():
         dsc = [torch.zeros(int(np.prod(h)), dtype=torch.float32, device="cuda") for h in hb]
         hp = bfz.AdamW(step=5, **WL.HP)
         if route == "unfused":
-            gt = torch.empty(n, dtype=torch.float32, device="cuda")
-            bfz.pack_shard(plan, grads, gt)
-            bfz.adamw_fp8_step(p, gt, m, v, codes, sc, hp)
+            bfz.adamw_fp8_step(p, folded, m, v, codes, sc, hp)
             bfz.unpack_fp8(plan, codes, sc, d8, dsc)
         elif route == "fused":
             bfz.fold_adamw_fp8_step(plan, grads, p, m, v, codes, sc, hp)
