@@ -377,6 +377,12 @@ void ora_adamw(float* p, const float* g, float* m, float* v, int64_t n,
  * A tile that is all zero would give s = 0 and a division by zero;
  * [Int8AdamW, §4.2 and §5.1] guard that case by using a scale of 1, which
  * is taken here (test: amax == 0 exactly), and all its codes are +0.
+ * A tile whose amax is positive but at most 224 * 2^-149 makes amax / 448
+ * round to zero in binary32 -- the same division by zero for a nonzero
+ * tile, which the pages do not address.  Reading: its scale is 2^-149, the
+ * smallest positive binary32 (the floor the power-of-two rule below also
+ * stops at); then x / s = x * 2^149 is exact and at most 224 in magnitude,
+ * so every code is finite.
  * [ZeRO-FP8, "Summary"]: the new FP8 weights and scales come from the
  * updated FP32 master, one tile at a time.
  * Parity: pinned by invariants (max code = 448, error bound, idempotence,
@@ -416,6 +422,7 @@ void ora_quant_tiles_mode(const float* p, int64_t n_tiles, uint8_t* codes,
             continue;
         }
         float s = pow2 ? ora_pow2_scale(amax) : amax / 448.0f;
+        if (s == 0.0f) s = (float)ldexp(1.0, -149);  /* amax / 448 underflowed */
         scale_inv[t] = s;
         for (int64_t k = 0; k < ORA_TILE_ELEMS; ++k) {
             float y = x[k] / s;

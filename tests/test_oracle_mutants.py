@@ -41,6 +41,7 @@ MUTANTS = {
     "scale uses 240": (": amax / 448.0f;", ": amax / 240.0f;"),
     "quotient multiplies by the scale": ("float y = x[k] / s;", "float y = x[k] * s;"),
     "zero tile scale 0": ("scale_inv[t] = 1.0f;", "scale_inv[t] = 0.0f;"),
+    "underflowed scale kept at 0": ("if (s == 0.0f) s = (float)ldexp(1.0, -149);", ""),
     "amax ignores negatives": ("if (fabsf(x[k]) > amax) amax = fabsf(x[k]);", "if (x[k] > amax) amax = x[k];"),
     "quota rounds down": ("int64_t q = ceil_div(T, D);", "int64_t q = T / D + (T % D != 0 && T < D);"),
     "param-wise: smallest weight first": ("if (size > pick_size) { pick = p; pick_size = size; }",
@@ -80,7 +81,8 @@ def _pins():
         pins.append(lambda kind=kind: Q.test_invariants(o, kind))
         pins.append(lambda kind=kind: Q.test_same_layout_requant_is_idempotent(o, kind))
     pins += [lambda: Q.test_exact_grid_tile(o), lambda: Q.test_block_quantize_multiply_form(o),
-             lambda: Q.test_zero_tile_guard_and_padding(o), lambda: Q.test_pow2_scale_edges(o)]
+             lambda: Q.test_zero_tile_guard_and_padding(o), lambda: Q.test_pow2_scale_edges(o),
+             lambda: Q.test_scale_underflow_floor(o)]
     for kind in ("normal", "heavy", "wide"):
         pins.append(lambda kind=kind: Q.test_pow2_invariants(o, kind))
     pins += [lambda s=s: P.test_brute_force_ownership(o, s) for s in range(4)]

@@ -125,6 +125,31 @@ def test_zero_tile_guard_and_padding(ora):
     assert codes[T + 5] == 0x7E and (np.delete(codes[T:], 5) == 0).all()
 
 
+def test_scale_underflow_floor(ora):
+    """A nonzero tile whose amax / 448 rounds to zero in binary32 (amax at
+    most 224 * 2^-149) takes the scale 2^-149 instead of dividing by zero:
+    x / 2^-149 is then an exact integer of magnitude <= 224, so the codes
+    are torch's E4M3 cast of those integers (signed zero kept).  One step
+    above the threshold the plain amax / 448 applies again (and rounds to
+    the same 2^-149)."""
+    tiny = 2.0 ** -149
+    rng = np.random.default_rng(9)
+    x = np.zeros(3 * T, dtype=np.float32)
+    x[:T] = (rng.integers(-100, 101, T) * tiny).astype(np.float32)
+    x[0], x[1] = np.float32(100 * tiny), np.float32(-0.0)
+    x[T + 17] = np.float32(-224 * tiny)                 # the tie: 224 / 448 rounds to 0
+    x[2 * T + 5] = np.float32(225 * tiny)               # just above it
+    x[2 * T + 6] = np.float32(-3 * tiny)
+    codes, scale, _ = ora.quant_tiles(x)
+    assert np.float32(np.float32(224 * tiny) / np.float32(448.0)) == 0.0
+    assert scale[0] == np.float32(tiny) and scale[1] == np.float32(tiny)
+    assert scale[2] == np.float32(np.float32(225 * tiny) / np.float32(448.0)) == np.float32(tiny)
+    y = torch.from_numpy((x.astype(np.float64) / tiny).astype(np.float32))
+    want = y.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, want)
+    assert codes[1] == 0x80 and codes[T + 17] == 0xF6  # -224 = -1.75 * 2^7: E = 14, M = 6
+
+
 # ---- power-of-two scales ------------------------------------------------------
 
 @pytest.mark.parametrize("kind", ["normal", "heavy", "wide"])
