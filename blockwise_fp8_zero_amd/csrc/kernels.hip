@@ -255,9 +255,13 @@ __device__ __forceinline__ void step_tile(int64_t tile, float* __restrict__ mast
     for (int w = 1; w < kStepWaves; ++w) amax = fmaxf(amax, wave_amax[w]);
 
     // scale_inv = amax / 448 (or its power-of-two form); an all-zero tile
-    // takes 1 and codes 0.
+    // takes 1 and codes 0.  A nonzero amax of at most 224 * 2^-149 rounds
+    // amax / 448 to zero: such a tile takes 2^-149, the smallest positive
+    // binary32, so no code comes from a division by zero.
     const bool zero = amax == 0.0f;
-    const float scale = zero ? 1.0f : (s.pow2 ? pow2_scale(amax) : amax / 448.0f);
+    const float plain = amax / 448.0f;
+    const float scale = zero ? 1.0f
+                             : (s.pow2 ? pow2_scale(amax) : (plain == 0.0f ? 0x1p-149f : plain));
     if (threadIdx.x == 0) {
         if (scale_inv) scale_inv[tile] = scale;
         if (out.scale_cell) *out.scale_cell = scale;

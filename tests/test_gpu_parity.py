@@ -375,3 +375,69 @@ def test_misaligned_pointer_is_rejected():
     with pytest.raises(bfz.BfzError) as e:
         bfz.adamw_fp8_step(off, off, off, off, c[:16384], s, bfz.AdamW(step=1, **WL.HP))
     assert e.value.code == bfz.BFZ_EALIGN
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_subnormal_masters_and_edge_amax(pow2):
+    """Host-forced cases, bit-exact against the oracle through all routes:
+    the tile amax in the last valid cell next to the padding of edge tiles;
+    a tile of subnormal masters with zero gradient and state, which stays
+    subnormal, so amax / 448 underflows and the 2^-149 floor applies; a tile
+    where subnormal gradients meet subnormal masters; a normal expert."""
+    tiny = 2.0 ** -149
+    dims = [(1, 130, 200), (2, 128, 256)]
+    _say("subnormal masters and pad-adjacent amax, pow2", pow2)
+    rng = np.random.default_rng(55)
+    w0 = rng.normal(0, 0.02, (1, 130, 200))
+    w0[0, 129, 199], w0[0, 127, 199], w0[0, 129, 127] = 0.5, -0.4, 0.3
+    g0 = rng.normal(0, 1e-3, (1, 130, 200))
+    w1 = rng.normal(0, 0.02, (2, 128, 256))
+    g1 = rng.normal(0, 1e-3, (2, 128, 256))
+    w1[0, :, :128] = rng.integers(-200, 201, (128, 128)) * tiny      # underflowing tile
+    g1[0, :, :128] = 0.0
+    w1[0, :, 128:] = rng.integers(-2 ** 20, 2 ** 20, (128, 128)) * tiny
+    g1[0, :, 128:] = rng.integers(-1000, 1001, (128, 128)) * tiny
+    masters = [w0.astype(np.float32), w1.astype(np.float32)]
+    grads = [g0.astype(np.float32), g1.astype(np.float32)]
+    assert np.abs(masters[1][0, :, :128]).max() <= np.float32(224 * tiny)
+    q, owned, table = oracle.plan(dims, 1, 0)
+    p0 = oracle.pack(dims, masters, table)
+    gt = oracle.pack(dims, grads, table)
+    n = q * 16384
+    steps = (1, 2)
+    op, om, ov = p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    for t in steps:
+        ocodes, oscale, _ = oracle.step(op, gt, om, ov, oracle.hparams(step=t, **WL.HP), 1e-6, pow2)
+    assert (oscale[:q] > 0).all()
+    odst8 = [np.zeros(d, np.uint8) for d in dims]
+    odsc = [np.zeros((E, -(-H // 128), -(-W // 128)), np.float32) for E, H, W in dims]
+    oracle.unpack(dims, ocodes, oscale, table, odst8, odsc)
+    plan = bfz.Plan(dims, 1, 0)
+    g_dev = [torch.from_numpy(g.reshape(-1)).cuda() for g in grads]
+    gt_dev = torch.from_numpy(gt).cuda()
+    for route in ("unfused", "fused", "fused_unpack"):
+        p = torch.from_numpy(p0).cuda()
+        m = torch.zeros(n, dtype=torch.float32, device="cuda")
+        v = torch.zeros(n, dtype=torch.float32, device="cuda")
+        codes = torch.zeros(n, dtype=torch.uint8, device="cuda")
+        sc = torch.zeros(q, dtype=torch.float32, device="cuda")
+        d8 = [torch.zeros(int(np.prod(d)), dtype=torch.uint8, device="cuda") for d in dims]
+        dsc = [torch.zeros(x.size, dtype=torch.float32, device="cuda") for x in odsc]
+        for t in steps:
+            hp = bfz.AdamW(step=t, scale_pow2=pow2, **WL.HP)
+            if route == "unfused":
+                bfz.adamw_fp8_step(p, gt_dev, m, v, codes, sc, hp)
+            elif route == "fused":
+                bfz.fold_adamw_fp8_step(plan, g_dev, p, m, v, codes, sc, hp)
+            else:
+                bfz.fold_adamw_fp8_step_unpack(plan, g_dev, p, m, v, codes, sc, d8, dsc, hp)
+        if route != "fused_unpack":
+            bfz.unpack_fp8(plan, codes, sc, d8, dsc)
+        torch.cuda.synchronize()
+        for name, got, want in (("master", p, op), ("m", m, om), ("v", v, ov), ("codes", codes, ocodes),
+                                ("scale_inv", sc, oscale)):
+            g_np = got.cpu().numpy()
+            assert np.array_equal(g_np.view(np.uint8), want.view(np.uint8)), (route, name)
+        for k in range(len(dims)):
+            assert np.array_equal(d8[k].cpu().numpy(), odst8[k].reshape(-1)), (route, "fp8", k)
+            assert np.array_equal(dsc[k].cpu().numpy(), odsc[k].reshape(-1)), (route, "grid", k)
