@@ -338,6 +338,7 @@ def main():
                           "fused": "fold_adamw_fp8_step + unpack_fp8",
                           "fused_unpack": "fold_adamw_fp8_step_unpack"}[args.path],
         },
+        "valid_elems_per_s": valid / (ms_per_step * 1e-3),
         "step_hbm_GBps": whole_bytes / (ms_per_step * 1e-3) / 1e9,
         "step_hbm_frac": whole_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "step_kernel_ms": step_kernel_ms,
