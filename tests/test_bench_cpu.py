@@ -1,0 +1,38 @@
+"""bench.py's contract checks that need no GPU (CPU only)."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_timed_path_does_not_load_the_oracle():
+    """Only the cpu_baseline leg may load the oracle: importing bench and the
+    GPU workload driver it times must leave it unloaded."""
+    code = ("import sys; import bench; import tests.gpu_run; "
+            "assert not any(m == 'oracle' or m.startswith('oracle.') for m in sys.modules), "
+            "sorted(m for m in sys.modules if 'oracle' in m)")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-3000:]
+
+
+def test_traffic_is_reported_only_for_the_profiled_kernel_source(tmp_path, monkeypatch):
+    good = tmp_path / "good.md"
+    stale = tmp_path / "stale.md"
+    good.write_text(f"kernel_sha256: {bench.kernel_sha()}\ntraffic_bytes_per_launch: 2.5e+10\n")
+    stale.write_text("kernel_sha256: " + "0" * 64 + "\ntraffic_bytes_per_launch: 2.5e+10\n")
+    monkeypatch.setitem(bench.TRAFFIC_FILES, "step_kernel", str(good))
+    assert bench.measured_traffic("step_kernel") == 2.5e10
+    monkeypatch.setitem(bench.TRAFFIC_FILES, "step_kernel", str(stale))
+    assert bench.measured_traffic("step_kernel") is None
+    monkeypatch.setitem(bench.TRAFFIC_FILES, "step_kernel", str(tmp_path / "missing.md"))
+    assert bench.measured_traffic("step_kernel") is None
