@@ -131,6 +131,47 @@ def test_full_size_sampled(name, mode):
     _free()
 
 
+def _beyond_32bit():
+    """The 2.01B-element recipe over 264 matrices of 4096x4096: 270,336
+    tiles, 4.43B elements -- slot element offsets pass 2^31 (slot 131,072)
+    and 2^32 (slot 262,144), and so do the byte offsets of the codes."""
+    w = WL.large()
+    w.name, w.config, w.seed = "beyond_32bit", 6, 6
+    w.dims = [(1, 4096, 4096)] * 264
+    w.description = "264 matrices of 4096x4096 (4.43B elements), D=1, t=1000"
+    return w
+
+
+_BIG = {}
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_offsets_beyond_32_bits(mode):
+    w = _beyond_32bit()
+    _say("beyond 32-bit offsets:", w.description, "mode", mode)
+    g = GpuWorkload(w, mode=mode)
+    assert g.q * 16384 > 2 ** 32
+    g.load_state()
+    g.run_steps()
+    if "ora" not in _BIG:
+        slots = sorted(set(sample_slots(w, n_random=40)) |
+                       {131071, 131072, 262143, 262144, g.q - 1})
+        _BIG["slots"], _BIG["ora"] = slots, oracle_slots(w, slots)
+    slots, ora = _BIG["slots"], _BIG["ora"]
+    rep = _check(g.tiles(slots), ora, "beyond_32bit " + mode)
+    assert rep["exact"]
+    fp8, sc = g.rowmajor()
+    torch.cuda.synchronize()
+    for k, s in enumerate(slots):
+        p, e, i, j, vr, vc = (int(x) for x in ora["table"][k])
+        E, H, W = w.dims[p]
+        block = fp8[p].view(E, H, W)[e, 128 * i:128 * i + vr, 128 * j:128 * j + vc]
+        assert np.array_equal(block.cpu().numpy(), ora["codes"][k].reshape(128, 128)[:vr, :vc]), s
+        assert float(sc[p][(e * (H // 128) + i) * (W // 128) + j]) == float(ora["scale_inv"][k])
+    del g, fp8, sc
+    _free()
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_rank_decomposition_is_invariant(mode):
     """Every tile's result is independent of which rank owns it: the union
