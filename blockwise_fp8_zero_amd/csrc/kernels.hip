@@ -547,9 +547,37 @@ __global__ __launch_bounds__(kThreads) void transpose_pow2_kernel(
             }
         }
         uint8_t* q = args.codes[t.local] + out_row * H + kTileDim * i + r0;
-        if (nvalid == 16 && (reinterpret_cast<uintptr_t>(q) & 15u) == 0) {
+        // The row's 128-byte segment starts b bytes past a 4-byte boundary
+        // (odd H).  A full-height tile then stores aligned words built from
+        // this lane's codes and the last word of its left neighbour in the
+        // row (a shuffle within the 8 lanes); only the segment's first and
+        // last partial words go byte by byte.  Ragged tiles store bytes.
+        const uintptr_t seg = reinterpret_cast<uintptr_t>(q) - (uintptr_t)r0;
+        const int b = (int)(seg & 3u);
+        const uint32_t prev = (uint32_t)__shfl_up((int)o[3], 1, 8);
+        if (t.valid_rows == kTileDim && (seg & 15u) == 0) {
             const u32x4 y = {o[0], o[1], o[2], o[3]};
             __builtin_nontemporal_store(y, reinterpret_cast<u32x4*>(q));
+        } else if (t.valid_rows == kTileDim && b == 0) {
+            uint32_t* qw = reinterpret_cast<uint32_t*>(q);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) __builtin_nontemporal_store(o[k], qw + k);
+        } else if (t.valid_rows == kTileDim) {
+            // word k holds segment bytes r0 - b + 4k .. +3
+            uint32_t* qw = reinterpret_cast<uint32_t*>(q - b);
+            uint32_t wv[4];
+            wv[0] = __builtin_amdgcn_alignbyte(o[0], prev, (uint32_t)(4 - b));
+#pragma unroll
+            for (int k = 1; k < 4; ++k) wv[k] = __builtin_amdgcn_alignbyte(o[k], o[k - 1], (uint32_t)(4 - b));
+            if (k2 == 0) {
+                for (int l = b; l < 4; ++l) q[l - b] = (uint8_t)(wv[0] >> (8 * l));
+            } else {
+                __builtin_nontemporal_store(wv[0], qw);
+            }
+#pragma unroll
+            for (int k = 1; k < 4; ++k) __builtin_nontemporal_store(wv[k], qw + k);
+            if (k2 == 7)
+                for (int l = 0; l < b; ++l) q[16 - b + l] = (uint8_t)(o[3] >> (8 * (4 - b + l)));
         } else {
             for (int l = 0; l < nvalid; ++l) q[l] = (uint8_t)(o[l >> 2] >> (8 * (l & 3)));
         }
