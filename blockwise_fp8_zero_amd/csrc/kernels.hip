@@ -194,6 +194,9 @@ struct RowMajorCodes {
     int32_t ld;
     int16_t rows, cols;
     bool vec;             // W % 4 == 0 and the weight is 4-byte aligned
+    // Rows off a 4-byte boundary store bytes, through the cache: the L2
+    // merges them, and building aligned words with a lane shuffle (as the
+    // unfold and transpose kernels do) measured 1.5% slower here.
     __device__ __forceinline__ void put(int k, uint32_t word) const {
         const int r = k * 32 + (threadIdx.x >> 5), c = 4 * (threadIdx.x & 31);
         if (origin == nullptr || r >= rows) return;
@@ -352,44 +355,70 @@ __global__ __launch_bounds__(kStepThreads) void pack_kernel(const TileEntry* __r
 }
 
 // Unfold of codes and scales: one workgroup per owned slot.  Thread t moves
-// 16 codes (column block t % 8) of rows t / 8, t / 8 + 32, ...; 16-byte
-// stores when the destination rows allow it, bytes at ragged edges.
+// 16 codes (column block t % 8) of rows t / 8, t / 8 + 32, ...  A row of a
+// full-width tile goes out as one 16-byte store per lane when it starts on a
+// 16-byte boundary, as 4-byte words when on a 4-byte boundary, and otherwise
+// as aligned words built from the lane's codes and its left neighbour's last
+// word (a shuffle within the row's 8 lanes), with bytes only for the row's
+// two partial end words.  The word stores are ordinary cached stores: such a
+// row shares its end cache lines with the neighbouring tiles, and the L2
+// merges the halves (streaming stores of partial lines measured about 1.6x
+// slower).  Ragged-width tiles use the widest store each lane's piece allows.
 __global__ __launch_bounds__(kThreads) void unpack_kernel(const TileEntry* __restrict__ entries,
                                                           const uint8_t* __restrict__ codes,
                                                           const float* __restrict__ scale_inv,
                                                           UnpackArgs args) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const int64_t slot = blockIdx.x;
     const TileEntry t = entries[slot];
     if (t.local < 0) return;
-    const uint4* in = reinterpret_cast<const uint4*>(codes + slot * kTileElems);
+    const u32x4* in = reinterpret_cast<const u32x4*>(codes + slot * kTileElems);
     uint8_t* dst = args.codes[t.local] + t.base;
     const int c16 = threadIdx.x & 7;
     const int r0 = threadIdx.x >> 3;
     const int col = 16 * c16;
-    const uintptr_t addr = reinterpret_cast<uintptr_t>(args.codes[t.local]);
-    const bool vec16 = ((t.ld & 15) == 0) && ((addr & 15u) == 0);
-    const bool vec4 = ((t.ld & 3) == 0) && ((addr & 3u) == 0);
+    const bool full = t.valid_cols == kTileDim;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int r = r0 + 32 * k;
-        if (r >= t.valid_rows) break;
-        const uint4 x = in[r * 8 + c16];
+        if (r >= t.valid_rows) break;  // the same for the 8 lanes of a row
+        const u32x4 x = __builtin_nontemporal_load(in + r * 8 + c16);
+        const uint32_t o[4] = {x[0], x[1], x[2], x[3]};
         uint8_t* row = dst + (int64_t)r * t.ld + col;
-        if (col + 16 <= t.valid_cols && vec16) {
-            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-            const u32x4 y = {x.x, x.y, x.z, x.w};
-            __builtin_nontemporal_store(y, reinterpret_cast<u32x4*>(row));
-        } else if (col + 16 <= t.valid_cols && vec4) {
-            uint32_t* r4 = reinterpret_cast<uint32_t*>(row);
-            r4[0] = x.x;
-            r4[1] = x.y;
-            r4[2] = x.z;
-            r4[3] = x.w;
-        } else {
-            for (int b = 0; b < 16 && col + b < t.valid_cols; ++b) {
-                const uint32_t w = b < 4 ? x.x : b < 8 ? x.y : b < 12 ? x.z : x.w;
-                row[b] = (uint8_t)(w >> (8 * (b & 3)));
+        const uintptr_t seg = reinterpret_cast<uintptr_t>(row) - (uintptr_t)col;
+        const int b = (int)(seg & 3u);
+        const uint32_t prev = (uint32_t)__shfl_up((int)o[3], 1, 8);
+        const uintptr_t at = reinterpret_cast<uintptr_t>(row);
+        if (full && (seg & 15u) == 0) {
+            __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(row));
+        } else if (full && b == 0) {
+            uint32_t* rw = reinterpret_cast<uint32_t*>(row);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) rw[q] = o[q];
+        } else if (full) {
+            // word q holds row bytes col - b + 4q .. +3
+            uint32_t* rw = reinterpret_cast<uint32_t*>(row - b);
+            uint32_t wv[4];
+            wv[0] = __builtin_amdgcn_alignbyte(o[0], prev, (uint32_t)(4 - b));
+#pragma unroll
+            for (int q = 1; q < 4; ++q) wv[q] = __builtin_amdgcn_alignbyte(o[q], o[q - 1], (uint32_t)(4 - b));
+            if (c16 == 0) {
+                for (int l = b; l < 4; ++l) row[l - b] = (uint8_t)(wv[0] >> (8 * l));
+            } else {
+                rw[0] = wv[0];
             }
+#pragma unroll
+            for (int q = 1; q < 4; ++q) rw[q] = wv[q];
+            if (c16 == 7)
+                for (int l = 0; l < b; ++l) row[16 - b + l] = (uint8_t)(o[3] >> (8 * (4 - b + l)));
+        } else if (col + 16 <= t.valid_cols && (at & 15u) == 0) {
+            __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(row));
+        } else if (col + 16 <= t.valid_cols && (at & 3u) == 0) {
+            uint32_t* rw = reinterpret_cast<uint32_t*>(row);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) rw[q] = o[q];
+        } else {
+            for (int l = 0; l < 16 && col + l < t.valid_cols; ++l) row[l] = (uint8_t)(o[l >> 2] >> (8 * (l & 3)));
         }
     }
     if (threadIdx.x == 0) args.scale[t.local][t.scale_index] = scale_inv[slot];
@@ -551,7 +580,9 @@ __global__ __launch_bounds__(kThreads) void transpose_pow2_kernel(
         // (odd H).  A full-height tile then stores aligned words built from
         // this lane's codes and the last word of its left neighbour in the
         // row (a shuffle within the 8 lanes); only the segment's first and
-        // last partial words go byte by byte.  Ragged tiles store bytes.
+        // last partial words go byte by byte.  Off a 16-byte boundary the
+        // stores are cached, so the L2 can merge the segment's end lines
+        // with the neighbouring tiles' pieces.  Ragged tiles store bytes.
         const uintptr_t seg = reinterpret_cast<uintptr_t>(q) - (uintptr_t)r0;
         const int b = (int)(seg & 3u);
         const uint32_t prev = (uint32_t)__shfl_up((int)o[3], 1, 8);
@@ -561,7 +592,7 @@ __global__ __launch_bounds__(kThreads) void transpose_pow2_kernel(
         } else if (t.valid_rows == kTileDim && b == 0) {
             uint32_t* qw = reinterpret_cast<uint32_t*>(q);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) __builtin_nontemporal_store(o[k], qw + k);
+            for (int k = 0; k < 4; ++k) qw[k] = o[k];
         } else if (t.valid_rows == kTileDim) {
             // word k holds segment bytes r0 - b + 4k .. +3
             uint32_t* qw = reinterpret_cast<uint32_t*>(q - b);
@@ -572,10 +603,10 @@ __global__ __launch_bounds__(kThreads) void transpose_pow2_kernel(
             if (k2 == 0) {
                 for (int l = b; l < 4; ++l) q[l - b] = (uint8_t)(wv[0] >> (8 * l));
             } else {
-                __builtin_nontemporal_store(wv[0], qw);
+                qw[0] = wv[0];
             }
 #pragma unroll
-            for (int k = 1; k < 4; ++k) __builtin_nontemporal_store(wv[k], qw + k);
+            for (int k = 1; k < 4; ++k) qw[k] = wv[k];
             if (k2 == 7)
                 for (int l = 0; l < b; ++l) q[16 - b + l] = (uint8_t)(o[3] >> (8 * (4 - b + l)));
         } else {
