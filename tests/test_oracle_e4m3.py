@@ -99,3 +99,7 @@ def test_near_midpoint_flags(ora):
     assert not ora.e4m3_near_midpoint(1.0)
     assert not ora.e4m3_near_midpoint(448.0)
     assert ora.e4m3_near_midpoint(-0.0146484375)
+    # the window is relative to the midpoint: 5e-7 relative off 304 (between
+    # 288 and 320) is near, 5e-7 absolute off 2^-10 (between 0 and 2^-9) is not
+    assert ora.e4m3_near_midpoint(np.float32(304.0) * np.float32(1 + 5e-7))
+    assert not ora.e4m3_near_midpoint(np.float32(2.0 ** -10 + 5e-7))

@@ -41,6 +41,11 @@ MUTANTS = {
     "scale uses 240": (": amax / 448.0f;", ": amax / 240.0f;"),
     "quotient multiplies by the scale": ("float y = x[k] / s;", "float y = x[k] * s;"),
     "zero tile scale 0": ("scale_inv[t] = 1.0f;", "scale_inv[t] = 0.0f;"),
+    "midpoint window absolute": ("return fabs(a - mid) <= rel * mid;", "return fabs(a - mid) <= rel;"),
+    "power-of-two scale floor at the smallest normal": ("    int T = -149;\n    while (ldexp(448.0, T) < (double)amax) ++T;",
+                                                         "    int T = -126;\n    while (ldexp(448.0, T) < (double)amax) ++T;"),
+    "transpose: groups keep the tile scale": ("double g = amax == 0.0 ? 1.0 : pow2_scale_d(amax);",
+                                              "double g = amax == 0.0 ? 1.0 : tile_scale;"),
     "underflowed scale kept at 0": ("if (s == 0.0f) s = (float)ldexp(1.0, -149);", ""),
     "amax ignores negatives": ("if (fabsf(x[k]) > amax) amax = fabsf(x[k]);", "if (x[k] > amax) amax = x[k];"),
     "quota rounds down": ("int64_t q = ceil_div(T, D);", "int64_t q = T / D + (T % D != 0 && T < D);"),
