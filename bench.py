@@ -175,10 +175,10 @@ def time_transpose(g, t, steps, stream):
     import torch
 
     import blockwise_fp8_zero_amd as bfz
-    pow2_was = g.pow2
-    g.pow2 = True
+    pow2_was, tile_codes_was = g.pow2, g.tile_codes
+    g.pow2, g.tile_codes = True, True  # the transpose reads the tile-major codes
     g.apply(t)
-    g.pow2 = pow2_was
+    g.pow2, g.tile_codes = pow2_was, tile_codes_was
     dims = g.w.dims
     dt = [None] * len(dims)
     ds = [None] * len(dims)
@@ -239,6 +239,9 @@ def main():
     log(f"workload {w.name}: {w.description}")
     t0 = time.perf_counter()
     g = GpuWorkload(w, mode=args.path, pow2=args.pow2)
+    # a lone rank (D = 1) gathers nothing: its one-kernel step writes only
+    # the row-major FP8 weights and scale grids, not the tile-major copy
+    lone = args.path == "fused_unpack" and w.D == 1
     g.load_state()
     prior = w.steps[:-1]
     if prior:
@@ -273,6 +276,7 @@ def main():
         if args.path != "fused_unpack":
             g.unpack(fp8, sc)
 
+    g.tile_codes = not lone
     for _ in range(args.warmup):
         one_step(t_next)
         t_next += 1
@@ -298,7 +302,11 @@ def main():
     kernel = KERNEL_OF_PATH[args.path]
     # fused kernels read the gradient of valid elements only
     grad_elems = elems if args.path == "unfused" else valid
-    algo_bytes = (STEP_BYTES_PER_ELEM - 4) * elems + 4 * grad_elems + STEP_BYTES_PER_TILE * g.q
+    # master, m, v read and written (24 B), the gradient read (4 B, valid
+    # elements only when read row-major), the tile-major code and scale
+    algo_bytes = (STEP_BYTES_PER_ELEM - 5) * elems + 4 * grad_elems
+    if not lone:
+        algo_bytes += elems + STEP_BYTES_PER_TILE * g.q
     if args.path == "fused_unpack":
         # row-major codes of the valid elements and the scale-grid cells
         algo_bytes += valid + 4 * g.owned
@@ -336,7 +344,8 @@ def main():
             "first_timed_step_t": w.measured_step + args.warmup,
             "step_path": {"unfused": "pack_shard(grad) + adamw_fp8_step + unpack_fp8",
                           "fused": "fold_adamw_fp8_step + unpack_fp8",
-                          "fused_unpack": "fold_adamw_fp8_step_unpack"}[args.path],
+                          "fused_unpack": "fold_adamw_fp8_step_unpack"}[args.path]
+                         + (" (row-major output only: D = 1)" if lone else ""),
         },
         "valid_elems_per_s": valid / (ms_per_step * 1e-3),
         "step_hbm_GBps": whole_bytes / (ms_per_step * 1e-3) / 1e9,

@@ -51,6 +51,9 @@ class GpuWorkload:
         self.codes = torch.empty(n, dtype=torch.uint8, **kw)
         self.scale_inv = torch.empty(self.q, dtype=torch.float32, **kw)
         self.grad_rm = None
+        # fused_unpack only: False = row-major output alone (a lone rank has
+        # nothing to all-gather, so no tile-major codes or scales)
+        self.tile_codes = True
         self.t_done = 0
         self.out_fp8 = self.out_scale = None
         if mode == "fused_unpack":
@@ -92,8 +95,9 @@ class GpuWorkload:
                                 self.scale_inv, hp_for(self.w, t, self.pow2))
 
     def fold_step_unpack(self, t):
+        codes, scale = (self.codes, self.scale_inv) if self.tile_codes else (None, None)
         bfz.fold_adamw_fp8_step_unpack(self.plan, self.grad_rm, self.master, self.m, self.v,
-                                       self.codes, self.scale_inv, self.out_fp8, self.out_scale,
+                                       codes, scale, self.out_fp8, self.out_scale,
                                        hp_for(self.w, t, self.pow2))
 
     def apply(self, t):

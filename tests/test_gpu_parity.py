@@ -131,6 +131,37 @@ def test_full_size_sampled(name, mode):
     _free()
 
 
+def test_lone_rank_rowmajor_only_full_size():
+    """The 2.01B-element workload (D = 1) as the bench steps it: the
+    one-kernel step with no tile-major codes or scales, only the row-major
+    FP8 weights and scale grids -- checked at the sampled tiles, with the
+    master / moments, against the oracle."""
+    w = WL.large()
+    _say("large, row-major output only (lone rank), full size")
+    g = GpuWorkload(w, mode="fused_unpack")
+    g.tile_codes = False
+    g.codes.fill_(0xAB)
+    g.scale_inv.fill_(-7.0)
+    g.load_state()
+    g.run_steps()
+    slots = sample_slots(w)
+    ora = oracle_slots(w, slots)
+    got = g.tiles(slots)
+    assert (got["codes"] == 0xAB).all() and (got["scale_inv"] == -7.0).all()  # untouched
+    for name in ("master", "m", "v"):
+        assert np.array_equal(got[name].view(np.uint32), ora[name].view(np.uint32)), name
+    fp8, sc = g.rowmajor()
+    torch.cuda.synchronize()
+    for k, s in enumerate(slots):
+        p, e, i, j, vr, vc = (int(x) for x in ora["table"][k])
+        E, H, W = w.dims[p]
+        block = fp8[p].view(E, H, W)[e, 128 * i:128 * i + vr, 128 * j:128 * j + vc]
+        assert np.array_equal(block.cpu().numpy(), ora["codes"][k].reshape(128, 128)[:vr, :vc]), s
+        assert float(sc[p][(e * (H // 128) + i) * (W // 128) + j]) == float(ora["scale_inv"][k])
+    del g, fp8, sc
+    _free()
+
+
 def _beyond_32bit():
     """The 2.01B-element recipe over 264 matrices of 4096x4096: 270,336
     tiles, 4.43B elements -- slot element offsets pass 2^31 (slot 131,072)
