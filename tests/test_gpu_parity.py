@@ -513,3 +513,40 @@ def test_subnormal_masters_and_edge_amax(pow2):
         for k in range(len(dims)):
             assert np.array_equal(d8[k].cpu().numpy(), odst8[k].reshape(-1)), (route, "fp8", k)
             assert np.array_equal(dsc[k].cpu().numpy(), odsc[k].reshape(-1)), (route, "grid", k)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_runs_on_the_callers_stream(mode):
+    """Every call is enqueued on the caller's current stream: a side stream
+    that waits for the set-up, takes all steps and is then waited for gives
+    bit for bit the default stream's result.  A call that went to another
+    stream would race with the set-up or the read-back."""
+    w = WL.ragged()
+    w.dims = w.dims[:12]
+    _say("side stream vs default stream, 12 ragged matrices, mode", mode)
+    outs = []
+    for side in (False, True):
+        g = GpuWorkload(w, mode=mode)
+        g.load_state()
+        if side:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                for t in w.steps:
+                    g.draw_grads(t)
+                    g.apply(t)
+                fp8, sc = g.rowmajor()
+            torch.cuda.current_stream().wait_stream(s)
+        else:
+            g.run_steps()
+            fp8, sc = g.rowmajor()
+        torch.cuda.synchronize()
+        tiles = g.tiles(list(range(g.q)))
+        outs.append((tiles, [x.cpu().numpy() if x is not None else None for x in fp8 + sc]))
+        del g
+        _free()
+    (ta, ra), (tb, rb) = outs
+    for k in ta:
+        assert np.array_equal(ta[k].view(np.uint8), tb[k].view(np.uint8)), k
+    for a, b in zip(ra, rb):
+        assert (a is None and b is None) or np.array_equal(a, b)
