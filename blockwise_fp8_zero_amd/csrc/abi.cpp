@@ -19,6 +19,19 @@ int hip_fail(const char* where, int err) {
     return fail(BFZ_EHIP, "%s: %s", where, hip_error_string(err));
 }
 
+// The plan's tile table lives on the device it was uploaded to: a call made
+// with another device current would hand that device a foreign pointer.
+int check_plan(const bfz_plan* plan, const char* where) {
+    if (!plan->d_entries) return fail(BFZ_ESTATE, "%s: plan not uploaded (bfz_plan_upload)", where);
+    int dev = -1;
+    const hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return hip_fail(where, err);
+    if (dev != plan->device)
+        return fail(BFZ_ESTATE, "%s: plan uploaded to device %d, but device %d is current", where,
+                    plan->device, dev);
+    return BFZ_OK;
+}
+
 // Owned slots reference only weights whose pointer must then be non-null.
 int check_weights(const bfz_plan* plan, const void* const* ptrs, const char* where) {
     for (const Segment& seg : plan->segments)
@@ -47,9 +60,10 @@ extern "C" const char* bfz_last_error(void) { return g_last_error; }
 
 extern "C" int pack_shard(const bfz_plan* plan, const float* const* src, float* dst, void* stream) {
     if (!plan || !src || !dst) return fail(BFZ_EINVAL, "pack_shard: null pointer");
-    if (!plan->d_entries) return fail(BFZ_ESTATE, "pack_shard: plan not uploaded (bfz_plan_upload)");
+    int rc = check_plan(plan, "pack_shard");
+    if (rc) return rc;
     if (!aligned(dst, 16)) return fail(BFZ_EALIGN, "pack_shard: dst must be 16-byte aligned");
-    int rc = check_weights(plan, reinterpret_cast<const void* const*>(src), "pack_shard");
+    rc = check_weights(plan, reinterpret_cast<const void* const*>(src), "pack_shard");
     if (rc) return rc;
     for (int32_t w = 0; w < plan->n_weights; ++w)
         if (src[w] && !aligned(src[w], 4))
@@ -68,10 +82,11 @@ extern "C" int unpack_fp8(const bfz_plan* plan, const uint8_t* codes, const floa
                           uint8_t* const* dst_fp8, float* const* dst_scale, void* stream) {
     if (!plan || !codes || !scale_inv || !dst_fp8 || !dst_scale)
         return fail(BFZ_EINVAL, "unpack_fp8: null pointer");
-    if (!plan->d_entries) return fail(BFZ_ESTATE, "unpack_fp8: plan not uploaded (bfz_plan_upload)");
+    int rc = check_plan(plan, "unpack_fp8");
+    if (rc) return rc;
     if (!aligned(codes, 16)) return fail(BFZ_EALIGN, "unpack_fp8: codes must be 16-byte aligned");
     if (!aligned(scale_inv, 4)) return fail(BFZ_EALIGN, "unpack_fp8: scale_inv must be 4-byte aligned");
-    int rc = check_weights(plan, reinterpret_cast<const void* const*>(dst_fp8), "unpack_fp8");
+    rc = check_weights(plan, reinterpret_cast<const void* const*>(dst_fp8), "unpack_fp8");
     if (rc) return rc;
     rc = check_weights(plan, reinterpret_cast<const void* const*>(dst_scale), "unpack_fp8 (scale)");
     if (rc) return rc;
@@ -151,9 +166,9 @@ extern "C" int fold_adamw_fp8_step(const bfz_plan* plan, const float* const* gra
                                    const bfz_adamw* hp, void* stream) {
     if (!plan || !grad || !master || !m || !v || !codes || !scale_inv || !hp)
         return fail(BFZ_EINVAL, "fold_adamw_fp8_step: null pointer");
-    if (!plan->d_entries)
-        return fail(BFZ_ESTATE, "fold_adamw_fp8_step: plan not uploaded (bfz_plan_upload)");
-    int rc = check_weights(plan, reinterpret_cast<const void* const*>(grad), "fold_adamw_fp8_step");
+    int rc = check_plan(plan, "fold_adamw_fp8_step");
+    if (rc) return rc;
+    rc = check_weights(plan, reinterpret_cast<const void* const*>(grad), "fold_adamw_fp8_step");
     if (rc) return rc;
     for (int32_t w = 0; w < plan->n_weights; ++w)
         if (grad[w] && !aligned(grad[w], 4))
@@ -184,8 +199,9 @@ extern "C" int fold_adamw_fp8_step_unpack(const bfz_plan* plan, const float* con
         return fail(BFZ_EINVAL, "%s: null pointer", where);
     if (!codes != !scale_inv)
         return fail(BFZ_EINVAL, "%s: codes and scale_inv must be both given or both NULL", where);
-    if (!plan->d_entries) return fail(BFZ_ESTATE, "%s: plan not uploaded (bfz_plan_upload)", where);
-    int rc = check_weights(plan, reinterpret_cast<const void* const*>(grad), where);
+    int rc = check_plan(plan, where);
+    if (rc) return rc;
+    rc = check_weights(plan, reinterpret_cast<const void* const*>(grad), where);
     if (!rc) rc = check_weights(plan, reinterpret_cast<const void* const*>(dst_fp8), where);
     if (!rc) rc = check_weights(plan, reinterpret_cast<const void* const*>(dst_scale), where);
     if (rc) return rc;
@@ -226,10 +242,11 @@ extern "C" int bfz_transpose_pow2(const bfz_plan* plan, const uint8_t* codes,
     const char* where = "bfz_transpose_pow2";
     if (!plan || !codes || !scale_inv || !dst_t || !dst_t_scale)
         return fail(BFZ_EINVAL, "%s: null pointer", where);
-    if (!plan->d_entries) return fail(BFZ_ESTATE, "%s: plan not uploaded (bfz_plan_upload)", where);
+    int rc = check_plan(plan, where);
+    if (rc) return rc;
     if (!aligned(codes, 16)) return fail(BFZ_EALIGN, "%s: codes must be 16-byte aligned", where);
     if (!aligned(scale_inv, 4)) return fail(BFZ_EALIGN, "%s: scale_inv must be 4-byte aligned", where);
-    int rc = check_weights(plan, reinterpret_cast<const void* const*>(dst_t), where);
+    rc = check_weights(plan, reinterpret_cast<const void* const*>(dst_t), where);
     if (!rc) rc = check_weights(plan, reinterpret_cast<const void* const*>(dst_t_scale), where);
     if (rc) return rc;
     for (int32_t w = 0; w < plan->n_weights; ++w)

@@ -49,7 +49,7 @@ extern "C" {
 #define BFZ_EINVAL (-1) /* null pointer, bad size or shape, bad hyper-parameter */
 #define BFZ_EALIGN (-2) /* a pointer lacks its required alignment */
 #define BFZ_EHIP (-3)   /* a HIP runtime call or kernel launch failed */
-#define BFZ_ESTATE (-4) /* plan used before bfz_plan_upload */
+#define BFZ_ESTATE (-4) /* plan not uploaded, or uploaded to another device than the current one */
 
 /* The block-wise split of one rank: the lookup table of its tiles. */
 typedef struct bfz_plan bfz_plan;
@@ -89,8 +89,10 @@ int bfz_plan_create(const int64_t* dims, int32_t n_params, int32_t D, int32_t ra
                     bfz_plan** out);
 
 /* Copy the plan's tile table to the current HIP device (allocates about
- * 24 bytes per tile; synchronous).  Needed once before pack_shard or
- * unpack_fp8.  Errors: BFZ_EINVAL (null), BFZ_EHIP. */
+ * 24 bytes per tile; synchronous).  Needed once before any call that takes
+ * the plan; those calls then require the same device to be current
+ * (BFZ_ESTATE otherwise).  Uploading again on the same device does nothing;
+ * on another device it is BFZ_EINVAL.  Errors: BFZ_EINVAL, BFZ_EHIP. */
 int bfz_plan_upload(bfz_plan* plan);
 
 /* Free the plan and its device table.  NULL is accepted. */

@@ -27,9 +27,10 @@
 #include "bfz_internal.h"
 
 // ---- the HIP runtime calls of the host code, on host memory ----------------
+static int g_device = 0;  // the "current device" the host code sees
 extern "C" {
 hipError_t hipGetDevice(int* d) {
-    *d = 0;
+    *d = g_device;
     return hipSuccess;
 }
 hipError_t hipSetDevice(int) { return hipSuccess; }
@@ -448,6 +449,19 @@ void run_error_paths() {
 
     CHECK(bfz_plan_create(dims, 1, 1, 0, &plan) == BFZ_OK && plan, "plan");
     CHECK(bfz_plan_upload(plan) == BFZ_OK, "upload");
+    {   // the plan belongs to the device it was uploaded on
+        const int64_t qq = bfz_plan_shard_tiles(plan);
+        float* d = exact<float>(qq * kTileElems);
+        float* wv = exact<float>(200 * 130);
+        const float* ws[1] = {wv};
+        g_device = 1;
+        CHECK(pack_shard(plan, ws, d, nullptr) == BFZ_ESTATE && std::strstr(bfz_last_error(), "device"),
+              "plan used with another device current");
+        CHECK(bfz_plan_upload(plan) == BFZ_EINVAL, "upload to a second device");
+        g_device = 0;
+        std::free(d);
+        std::free(wv);
+    }
     const int64_t q = bfz_plan_shard_tiles(plan), ne = q * kTileElems;
     float* a = exact<float>(ne + 4);
     uint8_t* c = exact<uint8_t>(ne + 16);
