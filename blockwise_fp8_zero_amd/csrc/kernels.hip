@@ -627,13 +627,14 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const float* __restric
 namespace {
 
 // The dynamic-LDS limit is a per-device function attribute: set it once per
-// kernel on each device the step runs on.
+// kernel on each device the step runs on (devices 0-63 remember it in a bit
+// mask; a device past 63 sets it on every launch, which is harmless).
 hipError_t reserve_lds(const void* kernel, std::atomic<uint64_t>& ready) {
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
-    const uint64_t bit = uint64_t(1) << (dev & 63);
-    if (!(ready.load(std::memory_order_acquire) & bit)) {
+    const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
+    if (!bit || !(ready.load(std::memory_order_acquire) & bit)) {
         err = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kStepLdsBytes);
         if (err != hipSuccess) return err;
         ready.fetch_or(bit, std::memory_order_release);
