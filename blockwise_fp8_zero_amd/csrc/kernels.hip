@@ -378,11 +378,16 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const TileEntry* __res
     const int r0 = threadIdx.x >> 3;
     const int col = 16 * c16;
     const bool full = t.valid_cols == kTileDim;
+    // all four row pieces are loaded before any store (the tile always holds
+    // 128 rows, padding included, so every load is in bounds)
+    u32x4 xs[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) xs[k] = __builtin_nontemporal_load(in + (r0 + 32 * k) * 8 + c16);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int r = r0 + 32 * k;
         if (r >= t.valid_rows) break;  // the same for the 8 lanes of a row
-        const u32x4 x = __builtin_nontemporal_load(in + r * 8 + c16);
+        const u32x4 x = xs[k];
         const uint32_t o[4] = {x[0], x[1], x[2], x[3]};
         uint8_t* row = dst + (int64_t)r * t.ld + col;
         const uintptr_t seg = reinterpret_cast<uintptr_t>(row) - (uintptr_t)col;
