@@ -139,12 +139,20 @@ def cpu_baseline(w, target_s=10.0):
     one_pass(st)
     per_pass = time.perf_counter() - t0
     passes = max(1, int(round(target_s / per_pass)))
-    # a one-thread figure on the same slab, about a tenth of the threaded time
-    passes1 = max(1, int(round(0.1 * target_s / per_pass)))
+    # a one-thread figure over a 1 GiB tile subset (16384 tiles of master,
+    # the slab's state in 64 separate copies, so the data lives in DRAM, not
+    # in the caches), one pass over each copy
+    copies = [new_state() for _ in range(max(1, 16384 // q))]
+    for c in copies:  # take the page faults of the fresh buffers now
+        for k, a in enumerate(c):
+            if k != 1:  # c[1] holds the folded master
+                a.fill(0)
     t0 = time.perf_counter()
-    for _ in range(passes1):
-        one_pass(st)
-    one_thread = passes1 * n / (time.perf_counter() - t0)
+    for c in copies:
+        one_pass(c)
+    one_thread = len(copies) * n / (time.perf_counter() - t0)
+    one_thread_gib = len(copies) * n * 4 / 2 ** 30
+    del copies
     states = [new_state() for _ in range(threads)]
 
     def work(k, count):
@@ -160,7 +168,10 @@ def cpu_baseline(w, target_s=10.0):
         dt = time.perf_counter() - t0
     elems = threads * passes * n
     return {"value": elems / dt, "unit": "elem/s", "cores": threads, "kind": "oracle",
-            "one_thread_value": one_thread, "nproc": os.cpu_count(), "cpu_model": cpu_model(),
+            "one_thread_value": one_thread,
+            "one_thread_sample": f"one thread, one pass over {one_thread_gib:.2f} GiB of master "
+                                 f"(the slab's state in {16384 // q} copies)",
+            "nproc": os.cpu_count(), "cpu_model": cpu_model(),
             "sample": f"fold + AdamW/E4M3 step + unfold of a {H}x{W} slab (256 tiles, "
                       f"{n / 1e6:.1f}M elements) of the first dense-LLM weight at t="
                       f"{w.measured_step}, {passes} passes on each of {threads} threads, "
