@@ -131,3 +131,12 @@ def test_pack_unpack_errors_without_gpu():
     assert L.bfz_e4m3_encode(C.c_void_p(0x10), C.c_void_p(0x10), -1, None) == bfz.BFZ_EINVAL
     assert L.bfz_plan_tile(p.handle, 99, C.cast((C.c_int64 * 6)(), C.c_void_p)) == bfz.BFZ_EINVAL
     p.close()
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without libbfz.so every call raises: there is no non-HIP fallback."""
+    import blockwise_fp8_zero_amd as bfz
+    monkeypatch.setattr(bfz, "LIB_PATH", str(tmp_path / "libbfz.so"))
+    monkeypatch.setattr(bfz, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        bfz.Plan([(1, 128, 128)], 1, 0)
