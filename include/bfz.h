@@ -150,7 +150,9 @@ int pack_shard(const bfz_plan* plan, const float* const* src, float* dst, void* 
  *                       p = p - (lr / (1 - b1^t)) m / (sqrt(v) / sqrt(1 - b2^t) + eps)
  *                       p = p - lr wd p          (when wd != 0; on the updated p)
  *   per tile:           amax = max |p|;  scale_inv = amax / 448 (or its power-of-two
- *                       form, see bfz_adamw.scale_pow2), or 1 when amax == 0
+ *                       form, see bfz_adamw.scale_pow2), or 1 when amax == 0, or
+ *                       2^-149 when amax / 448 rounds to zero in FP32
+ *                       (0 < amax <= 224 * 2^-149: subnormal tiles)
  *   per element:        code = E4M3(p / scale_inv), 0 in an all-zero tile,
  * where E4M3 is round-to-nearest (ties to even) onto the OCP E4M3FN values,
  * saturating at +-448, keeping the sign (tiny negatives give 0x80).
@@ -218,8 +220,10 @@ int fold_adamw_fp8_step_unpack(const bfz_plan* plan, const float* const* grad, f
  * grid [E, hb, wb]).  Elements of tiles other ranks own are not touched.
  * codes: q * 16384 bytes (16-byte aligned); scale_inv: q floats.
  * dst_fp8 / dst_scale: host arrays of n_params device pointers; entries of
- * weights the rank does not touch may be NULL.  Any alignment is accepted
- * (16-byte aligned rows take the vector path).
+ * weights the rank does not touch may be NULL.  Any alignment is accepted:
+ * rows take 16-byte stores where they start on a 16-byte boundary, aligned
+ * 32-bit words otherwise (bytes only at the ends of rows that start off a
+ * 4-byte boundary).
  * Errors: BFZ_EINVAL, BFZ_EALIGN, BFZ_ESTATE, BFZ_EHIP.
  */
 int unpack_fp8(const bfz_plan* plan, const uint8_t* codes, const float* scale_inv,
