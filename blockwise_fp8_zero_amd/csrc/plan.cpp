@@ -42,8 +42,9 @@ extern "C" int bfz_plan_create(const int64_t* dims, int32_t n_weights, int32_t D
             return fail(BFZ_EINVAL, "bfz_plan_create: weight %d has bad dims {%lld, %lld, %lld}", p,
                         (long long)E, (long long)H, (long long)W);
         int64_t grid = ceil_div(H, kTileDim) * ceil_div(W, kTileDim);
-        if (E > (int64_t(1) << 40) / grid)
-            return fail(BFZ_EINVAL, "bfz_plan_create: weight %d has too many tiles", p);
+        // a tile's cell in its weight's scale grid is a 32-bit index
+        if (E > int64_t(INT32_MAX) / grid)
+            return fail(BFZ_EINVAL, "bfz_plan_create: weight %d has more than 2^31 - 1 tiles", p);
         total += E * grid;
     }
 

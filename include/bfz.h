@@ -82,8 +82,8 @@ typedef struct {
  * the largest one; the contiguous equal quota is this library's reading of
  * how the page deals tiles to ranks).  Host only: touches no GPU.
  * On success *out receives a new plan.  Errors: BFZ_EINVAL for null
- * pointers, n_params < 1, D < 1, rank outside [0, D), a dimension < 1, or
- * H, W > 2^31 - 1.
+ * pointers, n_params < 1, D < 1, rank outside [0, D), a dimension < 1,
+ * H, W > 2^31 - 1, or a weight of more than 2^31 - 1 tiles.
  */
 int bfz_plan_create(const int64_t* dims, int32_t n_params, int32_t D, int32_t rank,
                     bfz_plan** out);

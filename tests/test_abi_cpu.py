@@ -76,6 +76,7 @@ def test_paramwise_split_matches_oracle():
 @pytest.mark.parametrize("dims,D,rank", [
     ([(1, 10, 10)], 0, 0), ([(1, 10, 10)], 2, 2), ([(1, 10, 10)], 2, -1),
     ([(0, 10, 10)], 1, 0), ([(1, 10, -3)], 1, 0), ([(1, 2 ** 31, 5)], 1, 0), ([], 1, 0),
+    ([(2 ** 20, 8192, 8192)], 4096, 0),  # 2^32 tiles: the scale-grid index would overflow
 ])
 def test_plan_rejects_bad_arguments(dims, D, rank):
     with pytest.raises(bfz.BfzError) as e:
