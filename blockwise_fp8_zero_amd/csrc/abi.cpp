@@ -19,10 +19,18 @@ int hip_fail(const char* where, int err) {
     return fail(BFZ_EHIP, "%s: %s", where, hip_error_string(err));
 }
 
+// One tile per 1024-thread workgroup, and a launch's work-item count is a
+// 32-bit number: at most this many tiles per launch.
+constexpr int64_t kMaxLaunchTiles = (int64_t(1) << 32) / 1024 - 1;
+
 // The plan's tile table lives on the device it was uploaded to: a call made
 // with another device current would hand that device a foreign pointer.
 int check_plan(const bfz_plan* plan, const char* where) {
     if (!plan->d_entries) return fail(BFZ_ESTATE, "%s: plan not uploaded (bfz_plan_upload)", where);
+    for (const Segment& seg : plan->segments)
+        if (seg.n_slots > kMaxLaunchTiles)
+            return fail(BFZ_EINVAL, "%s: %lld slots in one launch segment, more than %lld", where,
+                        (long long)seg.n_slots, (long long)kMaxLaunchTiles);
     int dev = -1;
     const hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return hip_fail(where, err);
@@ -147,8 +155,9 @@ extern "C" int adamw_fp8_step(float* master, const float* grad, float* m, float*
                               const bfz_adamw* hp, void* stream) {
     if (!master || !grad || !m || !v || !codes || !scale_inv || !hp)
         return fail(BFZ_EINVAL, "adamw_fp8_step: null pointer");
-    if (n_tiles < 0 || n_tiles > 0x7FFFFFFF)
-        return fail(BFZ_EINVAL, "adamw_fp8_step: n_tiles %lld outside [0, 2^31)", (long long)n_tiles);
+    if (n_tiles < 0 || n_tiles > kMaxLaunchTiles)
+        return fail(BFZ_EINVAL, "adamw_fp8_step: n_tiles %lld outside [0, %lld]", (long long)n_tiles,
+                    (long long)kMaxLaunchTiles);
     if (!aligned(grad, 16))
         return fail(BFZ_EALIGN, "adamw_fp8_step: master, grad, m, v and codes must be 16-byte aligned");
     int rc = check_state(master, m, v, codes, scale_inv, "adamw_fp8_step");

@@ -163,8 +163,9 @@ int pack_shard(const bfz_plan* plan, const float* const* src, float* dst, void* 
  * master, m, v: read and overwritten in place (16-byte aligned).
  * grad: read only (16-byte aligned).  codes: n_tiles * 16384 bytes written
  * (16-byte aligned).  scale_inv: n_tiles floats written (4-byte aligned).
- * n_tiles = 0 is a no-op.  Padding tiles (all zero) stay zero and give
- * scale_inv 1 and codes 0.
+ * n_tiles = 0 is a no-op; at most 4,194,303 tiles per call (one 1024-thread
+ * workgroup per tile, and a launch counts its work-items in 32 bits).
+ * Padding tiles (all zero) stay zero and give scale_inv 1 and codes 0.
  * Errors: BFZ_EINVAL (null pointer, n_tiles < 0, bad hyper-parameters),
  *         BFZ_EALIGN, BFZ_EHIP.
  */

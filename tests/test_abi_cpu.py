@@ -95,6 +95,7 @@ def test_step_argument_errors_without_gpu():
     assert _call_step([0] + ok[1:]) == bfz.BFZ_EINVAL
     assert _call_step(ok, n_tiles=-1) == bfz.BFZ_EINVAL
     assert _call_step(ok, n_tiles=1 << 31) == bfz.BFZ_EINVAL
+    assert _call_step(ok, n_tiles=(1 << 22)) == bfz.BFZ_EINVAL  # past 2^32 work-items
     for k in range(5):
         bad = list(ok)
         bad[k] += 4
