@@ -7,6 +7,8 @@ grid.  --path picks how:
   fused_unpack (default): fold_adamw_fp8_step_unpack -- all of it in one
       kernel, writing the tile-major codes/scales (the all-gather payload)
       and the row-major FP8 weights/scale grids;
+  fused_unpack_t: fold_adamw_fp8_step_unpack_t -- the same with power-of-two
+      scales, also writing the transposed copy W^T and its group scales;
   fused:   fold_adamw_fp8_step, then unpack_fp8;
   unfused: pack_shard, adamw_fp8_step, unpack_fp8.
 The split itself (the planner) runs once at set-up.
@@ -48,7 +50,8 @@ UNPACK_BYTES_PER_TILE = 8         # read + write scale
 TRAFFIC_FILES = {k: os.path.join(ROOT, "profiles", f"{k}_dense_llm_traffic.md")
                  for k in ("fold_step_unfold_kernel", "fold_step_kernel", "step_kernel",
                            "transpose_pow2_kernel")}
-KERNEL_OF_PATH = {"fused_unpack": "fold_step_unfold_kernel", "fused": "fold_step_kernel",
+KERNEL_OF_PATH = {"fused_unpack": "fold_step_unfold_kernel",
+                  "fused_unpack_t": "fold_step_unfold_t_kernel", "fused": "fold_step_kernel",
                   "unfused": "step_kernel"}
 KERNEL_SRC = os.path.join(ROOT, "blockwise_fp8_zero_amd", "csrc", "kernels.hip")
 
@@ -249,16 +252,21 @@ def main():
     w = WL.BY_NAME[args.workload]()
     log(f"workload {w.name}: {w.description}")
     t0 = time.perf_counter()
-    g = GpuWorkload(w, mode=args.path, pow2=args.pow2)
+    # fused_unpack_t: the one-kernel step with power-of-two scales that also
+    # writes the transposed copy W^T
+    transposed = args.path == "fused_unpack_t"
+    one_kernel = args.path in ("fused_unpack", "fused_unpack_t")
+    g = GpuWorkload(w, mode="fused_unpack" if one_kernel else args.path,
+                    pow2=args.pow2 or transposed, transposed=transposed)
     # a lone rank (D = 1) gathers nothing: its one-kernel step writes only
     # the row-major FP8 weights and scale grids, not the tile-major copy
-    lone = args.path == "fused_unpack" and w.D == 1
+    lone = one_kernel and w.D == 1
     g.load_state()
     prior = w.steps[:-1]
     if prior:
         g.run_steps(prior)
     g.draw_grads(w.measured_step)
-    fp8, sc = g.alloc_rowmajor_out() if args.path != "fused_unpack" else (None, None)
+    fp8, sc = g.alloc_rowmajor_out() if not one_kernel else (None, None)
     # a plain 1 GiB device copy, outside the timed region: the reference
     # kernel of known size for scaling the HBM byte counters
     a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -284,7 +292,7 @@ def main():
             g.fold_step_unpack(t)
         if ev is not None:
             ev[1].record(stream)
-        if args.path != "fused_unpack":
+        if not one_kernel:
             g.unpack(fp8, sc)
 
     g.tile_codes = not lone
@@ -318,16 +326,19 @@ def main():
     algo_bytes = (STEP_BYTES_PER_ELEM - 5) * elems + 4 * grad_elems
     if not lone:
         algo_bytes += elems + STEP_BYTES_PER_TILE * g.q
-    if args.path == "fused_unpack":
+    if one_kernel:
         # row-major codes of the valid elements and the scale-grid cells
         algo_bytes += valid + 4 * g.owned
+    if transposed:
+        # W^T codes of the valid elements, one scale per W^T row group
+        algo_bytes += valid + 4 * int(g.table[:g.owned, 5].sum())
     achieved = algo_bytes / (step_kernel_ms * 1e-3) / 1e9
     whole_bytes = algo_bytes
-    if args.path != "fused_unpack":
+    if not one_kernel:
         whole_bytes += UNPACK_BYTES_PER_ELEM * elems + UNPACK_BYTES_PER_TILE * g.q
     if args.path == "unfused":
         whole_bytes += PACK_BYTES_PER_ELEM * elems
-    traffic = measured_traffic(kernel) if w.name == "dense_llm" else None
+    traffic = measured_traffic(kernel) if w.name == "dense_llm" and kernel in TRAFFIC_FILES else None
     transpose = None
     if not args.skip_transpose:
         transpose = time_transpose(g, t_next, args.steps, stream)
@@ -355,7 +366,9 @@ def main():
             "first_timed_step_t": w.measured_step + args.warmup,
             "step_path": {"unfused": "pack_shard(grad) + adamw_fp8_step + unpack_fp8",
                           "fused": "fold_adamw_fp8_step + unpack_fp8",
-                          "fused_unpack": "fold_adamw_fp8_step_unpack"}[args.path]
+                          "fused_unpack": "fold_adamw_fp8_step_unpack",
+                          "fused_unpack_t": "fold_adamw_fp8_step_unpack_t (power-of-two scales, "
+                                            "plus the transposed copy W^T)"}[args.path]
                          + (" (row-major output only: D = 1)" if lone else ""),
         },
         "valid_elems_per_s": valid / (ms_per_step * 1e-3),

@@ -58,6 +58,8 @@ def lib():
         L.adamw_fp8_step.argtypes = [P, P, P, P, P, P, i64, C.POINTER(AdamW), P]
         L.fold_adamw_fp8_step.argtypes = [P, P, P, P, P, P, P, C.POINTER(AdamW), P]
         L.fold_adamw_fp8_step_unpack.argtypes = [P, P, P, P, P, P, P, P, P, C.POINTER(AdamW), P]
+        L.fold_adamw_fp8_step_unpack_t.argtypes = [P, P, P, P, P, P, P, P, P, P, P, C.POINTER(AdamW),
+                                                   P]
         L.unpack_fp8.argtypes = [P, P, P, P, P, P]
         L.bfz_e4m3_encode.argtypes = [P, P, i64, P]
         L.bfz_transpose_pow2.argtypes = [P, P, P, P, P, P]
@@ -232,6 +234,32 @@ def fold_adamw_fp8_step_unpack(plan: Plan, grads, master, m, v, codes, scale_inv
         plan.handle, C.cast(g, C.c_void_p), _dev(master, torch.float32, "master", q * TILE_ELEMS),
         _dev(m, torch.float32, "m", q * TILE_ELEMS), _dev(v, torch.float32, "v", q * TILE_ELEMS),
         c, sc, C.cast(a8, C.c_void_p), C.cast(asc, C.c_void_p), C.byref(hp), _stream(stream)))
+
+
+def fold_adamw_fp8_step_unpack_t(plan: Plan, grads, master, m, v, codes, scale_inv, dst_fp8,
+                                 dst_scale, dst_t, dst_t_scale, hp, stream=None):
+    """fold_adamw_fp8_step_unpack with power-of-two scales plus the transposed
+    copy (dst_t[p] uint8 (E, W, H), dst_t_scale[p] float32 (E, W, ceil(H/128)))
+    in one pass.  hp must have scale_pow2 set; codes / scale_inv may both be None."""
+    import torch
+    if isinstance(hp, dict):
+        hp = AdamW(**hp)
+    if (codes is None) != (scale_inv is None):
+        raise ValueError("codes and scale_inv: give both or neither")
+    n = len(plan.dims)
+    q = plan.shard_tiles
+    g = _ptr_array(grads, torch.float32, "grads", n)
+    a8 = _ptr_array(dst_fp8, torch.uint8, "dst_fp8", n)
+    asc = _ptr_array(dst_scale, torch.float32, "dst_scale", n)
+    t8 = _ptr_array(dst_t, torch.uint8, "dst_t", n)
+    tsc = _ptr_array(dst_t_scale, torch.float32, "dst_t_scale", n)
+    c = None if codes is None else _dev(codes, torch.uint8, "codes", q * TILE_ELEMS)
+    sc = None if scale_inv is None else _dev(scale_inv, torch.float32, "scale_inv", q)
+    _check(lib().fold_adamw_fp8_step_unpack_t(
+        plan.handle, C.cast(g, C.c_void_p), _dev(master, torch.float32, "master", q * TILE_ELEMS),
+        _dev(m, torch.float32, "m", q * TILE_ELEMS), _dev(v, torch.float32, "v", q * TILE_ELEMS),
+        c, sc, C.cast(a8, C.c_void_p), C.cast(asc, C.c_void_p), C.cast(t8, C.c_void_p),
+        C.cast(tsc, C.c_void_p), C.byref(hp), _stream(stream)))
 
 
 def unpack_fp8(plan: Plan, codes, scale_inv, dst_fp8, dst_scale, stream=None):

@@ -245,6 +245,66 @@ extern "C" int fold_adamw_fp8_step_unpack(const bfz_plan* plan, const float* con
     return BFZ_OK;
 }
 
+extern "C" int fold_adamw_fp8_step_unpack_t(const bfz_plan* plan, const float* const* grad,
+                                            float* master, float* m, float* v, uint8_t* codes,
+                                            float* scale_inv, uint8_t* const* dst_fp8,
+                                            float* const* dst_scale, uint8_t* const* dst_t,
+                                            float* const* dst_t_scale, const bfz_adamw* hp,
+                                            void* stream) {
+    const char* where = "fold_adamw_fp8_step_unpack_t";
+    if (!plan || !grad || !master || !m || !v || !dst_fp8 || !dst_scale || !dst_t || !dst_t_scale ||
+        !hp)
+        return fail(BFZ_EINVAL, "%s: null pointer", where);
+    if (!codes != !scale_inv)
+        return fail(BFZ_EINVAL, "%s: codes and scale_inv must be both given or both NULL", where);
+    if (!hp->scale_pow2)
+        return fail(BFZ_EINVAL, "%s: the transposed copy needs power-of-two scales (scale_pow2)",
+                    where);
+    int rc = check_plan(plan, where);
+    if (rc) return rc;
+    rc = check_weights(plan, reinterpret_cast<const void* const*>(grad), where);
+    if (!rc) rc = check_weights(plan, reinterpret_cast<const void* const*>(dst_fp8), where);
+    if (!rc) rc = check_weights(plan, reinterpret_cast<const void* const*>(dst_scale), where);
+    if (!rc) rc = check_weights(plan, reinterpret_cast<const void* const*>(dst_t), where);
+    if (!rc) rc = check_weights(plan, reinterpret_cast<const void* const*>(dst_t_scale), where);
+    if (rc) return rc;
+    for (int32_t w = 0; w < plan->n_weights; ++w) {
+        if (grad[w] && !aligned(grad[w], 4))
+            return fail(BFZ_EALIGN, "%s: gradient %d must be 4-byte aligned", where, w);
+        if (dst_scale[w] && !aligned(dst_scale[w], 4))
+            return fail(BFZ_EALIGN, "%s: scale grid %d must be 4-byte aligned", where, w);
+        if (dst_t_scale[w] && !aligned(dst_t_scale[w], 4))
+            return fail(BFZ_EALIGN, "%s: transposed scale grid %d must be 4-byte aligned", where, w);
+    }
+    if (!aligned(master, 16) || !aligned(m, 16) || !aligned(v, 16) || (codes && !aligned(codes, 16)))
+        return fail(BFZ_EALIGN, "%s: master, m, v and codes must be 16-byte aligned", where);
+    if (scale_inv && !aligned(scale_inv, 4))
+        return fail(BFZ_EALIGN, "%s: scale_inv must be 4-byte aligned", where);
+    StepScalars s;
+    rc = make_scalars(hp, &s, where);
+    if (rc) return rc;
+    for (const Segment& seg : plan->segments) {
+        PackArgs in{};
+        UnpackArgs out{};
+        TransposeArgs tout{};
+        for (int32_t k = 0; k < seg.n_weights; ++k) {
+            in.src[k] = grad[seg.weight0 + k];
+            out.codes[k] = dst_fp8[seg.weight0 + k];
+            out.scale[k] = dst_scale[seg.weight0 + k];
+            tout.codes[k] = dst_t[seg.weight0 + k];
+            tout.scale[k] = dst_t_scale[seg.weight0 + k];
+            tout.rows[k] = int32_t(plan->dims[3 * (seg.weight0 + k) + 1]);
+        }
+        const int64_t off = seg.slot0 * kTileElems;
+        int err = launch_fold_step_unfold_t(plan->d_entries + seg.slot0, seg.n_slots, in, out, tout,
+                                            master + off, m + off, v + off,
+                                            codes ? codes + off : nullptr,
+                                            scale_inv ? scale_inv + seg.slot0 : nullptr, s, stream);
+        if (err != hipSuccess) return hip_fail(where, err);
+    }
+    return BFZ_OK;
+}
+
 extern "C" int bfz_transpose_pow2(const bfz_plan* plan, const uint8_t* codes,
                                   const float* scale_inv, uint8_t* const* dst_t,
                                   float* const* dst_t_scale, void* stream) {

@@ -69,6 +69,10 @@ int launch_fold_step(const TileEntry* d_entries, int64_t n_slots, const PackArgs
 int launch_fold_step_unfold(const TileEntry* d_entries, int64_t n_slots, const PackArgs& grads,
                             const UnpackArgs& outs, float* master, float* m, float* v,
                             uint8_t* codes, float* scale_inv, const StepScalars& s, void* stream);
+int launch_fold_step_unfold_t(const TileEntry* d_entries, int64_t n_slots, const PackArgs& grads,
+                              const UnpackArgs& outs, const TransposeArgs& touts, float* master,
+                              float* m, float* v, uint8_t* codes, float* scale_inv,
+                              const StepScalars& s, void* stream);
 int launch_transpose_pow2(const TileEntry* d_entries, int64_t n_slots, const uint8_t* codes,
                           const float* scale_inv, const TransposeArgs& args, void* stream);
 int launch_encode(const float* in, uint8_t* out, int64_t n, void* stream);

@@ -211,13 +211,13 @@ struct RowMajorCodes {
     }
 };
 
-template <class GradFn>
-__device__ __forceinline__ void step_tile(int64_t tile, float* __restrict__ master,
-                                          float* __restrict__ mom1, float* __restrict__ mom2,
-                                          uint32_t* __restrict__ codes,
-                                          float* __restrict__ scale_inv, const StepScalars& s,
-                                          const GradFn& grad_at, float* wave_amax,
-                                          const RowMajorCodes& out = RowMajorCodes{}) {
+template <class GradFn, class Out = RowMajorCodes>
+__device__ __forceinline__ float step_tile(int64_t tile, float* __restrict__ master,
+                                           float* __restrict__ mom1, float* __restrict__ mom2,
+                                           uint32_t* __restrict__ codes,
+                                           float* __restrict__ scale_inv, const StepScalars& s,
+                                           const GradFn& grad_at, float* wave_amax,
+                                           const Out& out = Out{}) {
     const int64_t base = tile * (kTileElems / 4);
     f32x4* P = reinterpret_cast<f32x4*>(master) + base;
     f32x4* M = reinterpret_cast<f32x4*>(mom1) + base;
@@ -276,6 +276,7 @@ __device__ __forceinline__ void step_tile(int64_t tile, float* __restrict__ mast
         if (C) store_stream(C + k * kStepThreads + threadIdx.x, word);
         out.put(k, word);
     }
+    return scale;
 }
 
 __global__ __launch_bounds__(kStepThreads) void step_kernel(
@@ -481,6 +482,96 @@ __device__ __forceinline__ uint32_t mag_max16(const uint32_t v[4]) {
     return m;
 }
 
+// One lane's part of W^T row c of a tile: the lane holds bytes 16 k2 .. +15
+// of the row (tile rows 16 k2 .. +15 of column c) in v, 8 lanes per row.
+// The group's largest magnitude code (valid rows only; an 8-lane shuffle
+// reduction) gives the headroom d (clamped so 2^(T - d) >= 2^-149), lane 0
+// writes the group scale, and every code is moved up d binades: one add per
+// 32-bit word when the lane's codes are all normal or zero (8d on each
+// normal byte cannot carry out of it: the headroom keeps every code <= 126),
+// byte by byte when one is subnormal or on a ragged edge.  All 8 lanes of
+// the row must call it (shuffles).  An all-zero group: scale 1, codes 0.
+__device__ __forceinline__ void wt_row(const uint32_t v[4], int c, int k2, int T, const TileEntry& t,
+                                       uint8_t* wt, float* wt_scale, int64_t H, int64_t W,
+                                       int64_t hb, int64_t e, int64_t i, int64_t j) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const int r0 = 16 * k2;
+    const int nvalid = max(0, min(16, (int)t.valid_rows - r0));
+    uint32_t mx = 0;
+    if (nvalid == 16) {
+        mx = mag_max16(v);
+    } else {
+        for (int l = 0; l < nvalid; ++l) mx = max(mx, (v[l >> 2] >> (8 * (l & 3))) & 0x7Fu);
+    }
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1, 64));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2, 64));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 4, 64));
+    if (c >= t.valid_cols) return;
+    int d = mx == 0u ? 0 : e4m3_headroom(mx);
+    if (T - d < -149) d = T + 149;
+    const int64_t out_row = e * W + kTileDim * j + c;
+    if (k2 == 0) wt_scale[out_row * hb + i] = mx == 0u ? 1.0f : pow2_value(T - d);
+    if (nvalid == 0) return;
+    uint32_t o[4] = {0u, 0u, 0u, 0u};
+    if (mx != 0u) {
+        // per byte: bit 7 of nf set for a normal code (exponent field != 0);
+        // sub collects nonzero codes that are not normal
+        uint32_t nf[4], sub = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t a = v[q] & 0x7F7F7F7Fu;
+            nf[q] = ((a & 0x78787878u) + 0x78787878u) & 0x80808080u;
+            sub |= ((a + 0x7F7F7F7Fu) & 0x80808080u) & ~nf[q];
+        }
+        if (nvalid == 16 && sub == 0u) {
+            const uint32_t inc = (uint32_t)d << 3;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = v[q] + (nf[q] >> 7) * inc;
+        } else {
+            for (int l = 0; l < 16; ++l)
+                o[l >> 2] |= (l < nvalid ? e4m3_scale_up((v[l >> 2] >> (8 * (l & 3))) & 0xFFu, d) : 0u)
+                             << (8 * (l & 3));
+        }
+    }
+    uint8_t* q = wt + out_row * H + kTileDim * i + r0;
+    // The row's 128-byte segment starts b bytes past a 4-byte boundary
+    // (odd H).  A full-height tile then stores aligned words built from
+    // this lane's codes and the last word of its left neighbour in the
+    // row (a shuffle within the 8 lanes); only the segment's first and
+    // last partial words go byte by byte.  Off a 16-byte boundary the
+    // stores are cached, so the L2 can merge the segment's end lines
+    // with the neighbouring tiles' pieces.  Ragged tiles store bytes.
+    const uintptr_t seg = reinterpret_cast<uintptr_t>(q) - (uintptr_t)r0;
+    const int b = (int)(seg & 3u);
+    const uint32_t prev = (uint32_t)__shfl_up((int)o[3], 1, 8);
+    if (t.valid_rows == kTileDim && (seg & 15u) == 0) {
+        const u32x4 y = {o[0], o[1], o[2], o[3]};
+        __builtin_nontemporal_store(y, reinterpret_cast<u32x4*>(q));
+    } else if (t.valid_rows == kTileDim && b == 0) {
+        uint32_t* qw = reinterpret_cast<uint32_t*>(q);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) qw[k] = o[k];
+    } else if (t.valid_rows == kTileDim) {
+        // word k holds segment bytes r0 - b + 4k .. +3
+        uint32_t* qw = reinterpret_cast<uint32_t*>(q - b);
+        uint32_t wv[4];
+        wv[0] = __builtin_amdgcn_alignbyte(o[0], prev, (uint32_t)(4 - b));
+#pragma unroll
+        for (int k = 1; k < 4; ++k) wv[k] = __builtin_amdgcn_alignbyte(o[k], o[k - 1], (uint32_t)(4 - b));
+        if (k2 == 0) {
+            for (int l = b; l < 4; ++l) q[l - b] = (uint8_t)(wv[0] >> (8 * l));
+        } else {
+            qw[0] = wv[0];
+        }
+#pragma unroll
+        for (int k = 1; k < 4; ++k) qw[k] = wv[k];
+        if (k2 == 7)
+            for (int l = 0; l < b; ++l) q[16 - b + l] = (uint8_t)(o[3] >> (8 * (4 - b + l)));
+    } else {
+        for (int l = 0; l < nvalid; ++l) q[l] = (uint8_t)(o[l >> 2] >> (8 * (l & 3)));
+    }
+}
+
 // One 256-thread workgroup per owned slot.
 //  1. Thread t reads rows 4(t / 8) .. +3, bytes 16(t % 8) .. +15 of the tile
 //     (four 16-byte loads), transposes each 4x4-byte block with byte
@@ -491,14 +582,7 @@ __device__ __forceinline__ uint32_t mag_max16(const uint32_t v[4]) {
 //     exactly two lanes of a wave on every bank in step 1.
 //  2. Eight consecutive lanes own one W^T row, 16 bytes (one aligned 16-byte
 //     LDS read) each, so a wave stores eight contiguous 128-byte row
-//     segments.  The group's largest magnitude code (valid rows only) is an
-//     8-lane shuffle reduction; it gives the headroom d (clamped so
-//     2^(T - d) >= 2^-149), every code is moved up d binades, and lane 0 of
-//     the row writes the group scale.  When a lane's 16 codes are all normal
-//     or zero, the move is one add per word: 8d on the exponent field of each
-//     normal byte (d never carries out of a byte: the headroom keeps every
-//     code <= 126); codes with a subnormal, and ragged edges, go byte by byte.
-// An all-zero column: scale 1, codes 0.
+//     segments (wt_row: group scale, exponent edit, store).
 __global__ __launch_bounds__(kThreads) void transpose_pow2_kernel(
     const TileEntry* __restrict__ entries, const uint8_t* __restrict__ codes,
     const float* __restrict__ scale_inv, TransposeArgs args) {
@@ -537,87 +621,97 @@ __global__ __launch_bounds__(kThreads) void transpose_pow2_kernel(
     const int64_t j = t.scale_index % wb, ei = t.scale_index / wb;
     const int64_t i = ei % hb, e = ei / hb;
     const int k2 = threadIdx.x & 7;        // 16-byte chunk of the row: rows 16 k2 .. +15
-    const int r0 = 16 * k2;
-    const int nvalid = max(0, min(16, (int)t.valid_rows - r0));
 #pragma unroll
     for (int mr = 0; mr < 4; ++mr) {
         const int c = (threadIdx.x >> 3) + 32 * mr;  // W^T row within the tile
         const u32x4 vv = *reinterpret_cast<const u32x4*>(&tile_t[c * 32 + ((4 * k2 + 4 * (c >> 4)) & 31)]);
         const uint32_t v[4] = {vv[0], vv[1], vv[2], vv[3]};
-        uint32_t mx = 0;
-        if (nvalid == 16) {
-            mx = mag_max16(v);
-        } else {
-            for (int l = 0; l < nvalid; ++l) mx = max(mx, (v[l >> 2] >> (8 * (l & 3))) & 0x7Fu);
-        }
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1, 64));
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2, 64));
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 4, 64));
-        if (c >= t.valid_cols) continue;
-        int d = mx == 0u ? 0 : e4m3_headroom(mx);
-        if (T - d < -149) d = T + 149;
-        const int64_t out_row = e * W + kTileDim * j + c;
-        if (k2 == 0) args.scale[t.local][out_row * hb + i] = mx == 0u ? 1.0f : pow2_value(T - d);
-        if (nvalid == 0) continue;
-        uint32_t o[4] = {0u, 0u, 0u, 0u};
-        if (mx != 0u) {
-            // per byte: bit 7 of nf set for a normal code (exponent field != 0);
-            // sub collects nonzero codes that are not normal
-            uint32_t nf[4], sub = 0;
+        wt_row(v, c, k2, T, t, args.codes[t.local], args.scale[t.local], H, W, hb, e, i, j);
+    }
+}
+
+// Sink of the step's code words for the fused transposed copy: each word
+// goes to the row-major FP8 weight (as RowMajorCodes) and into an LDS copy
+// of the tile's codes, row r word w (columns 4w .. 4w + 3) at
+// r * 32 + ((w + r / 4) % 32); that rotation puts two lanes of a wave on
+// each bank both here and in the 4x4-block reads that follow.
+struct StagedCodes {
+    RowMajorCodes rm;
+    float* scale_cell;   // the row-major scale-grid cell (step_tile writes it)
+    uint32_t* tile_rm;   // LDS, 4096 words
+    __device__ __forceinline__ void put(int k, uint32_t word) const {
+        rm.put(k, word);
+        const int r = k * 32 + (threadIdx.x >> 5), w = threadIdx.x & 31;
+        tile_rm[r * 32 + ((w + (r >> 2)) & 31)] = word;
+    }
+};
+
+// Fold, power-of-two step, unfold and the transposed copy in one pass: as
+// fold_step_unfold_kernel, and each owned tile's codes also leave as W^T
+// (row-major [E, W, H]) with one power-of-two scale per 128-element group
+// of a W^T row, by exponent edits of the codes the step just produced --
+// the scaling-aware transpose without reading the codes back.
+//  1. the step (step_tile); its code words also go to LDS (StagedCodes);
+//  2. thread t transposes the 4x4-byte block of tile rows 4 (t % 32) .. +3,
+//     column word t / 32, into W^T-row words laid out as in
+//     transpose_pow2_kernel (two lanes per bank on both sides);
+//  3. 8 lanes per W^T row, the 1024 threads covering the tile's 128 columns
+//     at once: wt_row.
+__global__ __launch_bounds__(kStepThreads) void fold_step_unfold_t_kernel(
+    const TileEntry* __restrict__ entries, PackArgs grads, UnpackArgs outs, TransposeArgs touts,
+    float* __restrict__ master, float* __restrict__ mom1, float* __restrict__ mom2,
+    uint32_t* __restrict__ codes, float* __restrict__ scale_inv, StepScalars s, int64_t n_slots) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    extern __shared__ float smem[];
+    float* wave_amax = smem;                                       // kStepWaves floats
+    uint32_t* tile_rm = reinterpret_cast<uint32_t*>(smem + 64);    // 16 KiB, codes by rows
+    uint32_t* tile_t = tile_rm + kTileElems / 4;                   // 16 KiB, codes by W^T rows
+    const int64_t slot = xcd_tile(blockIdx.x, n_slots);
+    const TileEntry t = entries[slot];
+    RowMajorGrad g{nullptr, t.ld, t.valid_rows, t.valid_cols, false};
+    StagedCodes out{RowMajorCodes{nullptr, nullptr, t.ld, t.valid_rows, t.valid_cols, false}, nullptr,
+                    tile_rm};
+    if (t.local >= 0) {
+        const float* w = grads.src[t.local];
+        g.origin = w + t.base;
+        g.vec = ((t.ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(w) & 15u) == 0);
+        uint8_t* d = outs.codes[t.local];
+        out.rm.origin = d + t.base;
+        out.rm.vec = ((t.ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(d) & 3u) == 0);
+        out.scale_cell = outs.scale[t.local] + t.scale_index;
+    }
+    const float scale = step_tile(slot, master, mom1, mom2, codes, scale_inv, s, g, wave_amax, out);
+    __syncthreads();
+    {
+        const int rq = threadIdx.x & 31, bc = threadIdx.x >> 5;
+        uint32_t w[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t a = v[q] & 0x7F7F7F7Fu;
-                nf[q] = ((a & 0x78787878u) + 0x78787878u) & 0x80808080u;
-                sub |= ((a + 0x7F7F7F7Fu) & 0x80808080u) & ~nf[q];
-            }
-            if (nvalid == 16 && sub == 0u) {
-                const uint32_t inc = (uint32_t)d << 3;
+        for (int j = 0; j < 4; ++j) w[j] = tile_rm[(4 * rq + j) * 32 + ((bc + rq) & 31)];
+        const uint32_t x01lo = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);
+        const uint32_t x01hi = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);
+        const uint32_t x23lo = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+        const uint32_t x23hi = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+        const uint32_t col[4] = {__builtin_amdgcn_perm(x23lo, x01lo, 0x05040100u),
+                                 __builtin_amdgcn_perm(x23lo, x01lo, 0x07060302u),
+                                 __builtin_amdgcn_perm(x23hi, x01hi, 0x05040100u),
+                                 __builtin_amdgcn_perm(x23hi, x01hi, 0x07060302u)};
 #pragma unroll
-                for (int q = 0; q < 4; ++q) o[q] = v[q] + (nf[q] >> 7) * inc;
-            } else {
-                for (int l = 0; l < 16; ++l)
-                    o[l >> 2] |= (l < nvalid ? e4m3_scale_up((v[l >> 2] >> (8 * (l & 3))) & 0xFFu, d) : 0u)
-                                 << (8 * (l & 3));
-            }
-        }
-        uint8_t* q = args.codes[t.local] + out_row * H + kTileDim * i + r0;
-        // The row's 128-byte segment starts b bytes past a 4-byte boundary
-        // (odd H).  A full-height tile then stores aligned words built from
-        // this lane's codes and the last word of its left neighbour in the
-        // row (a shuffle within the 8 lanes); only the segment's first and
-        // last partial words go byte by byte.  Off a 16-byte boundary the
-        // stores are cached, so the L2 can merge the segment's end lines
-        // with the neighbouring tiles' pieces.  Ragged tiles store bytes.
-        const uintptr_t seg = reinterpret_cast<uintptr_t>(q) - (uintptr_t)r0;
-        const int b = (int)(seg & 3u);
-        const uint32_t prev = (uint32_t)__shfl_up((int)o[3], 1, 8);
-        if (t.valid_rows == kTileDim && (seg & 15u) == 0) {
-            const u32x4 y = {o[0], o[1], o[2], o[3]};
-            __builtin_nontemporal_store(y, reinterpret_cast<u32x4*>(q));
-        } else if (t.valid_rows == kTileDim && b == 0) {
-            uint32_t* qw = reinterpret_cast<uint32_t*>(q);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) qw[k] = o[k];
-        } else if (t.valid_rows == kTileDim) {
-            // word k holds segment bytes r0 - b + 4k .. +3
-            uint32_t* qw = reinterpret_cast<uint32_t*>(q - b);
-            uint32_t wv[4];
-            wv[0] = __builtin_amdgcn_alignbyte(o[0], prev, (uint32_t)(4 - b));
-#pragma unroll
-            for (int k = 1; k < 4; ++k) wv[k] = __builtin_amdgcn_alignbyte(o[k], o[k - 1], (uint32_t)(4 - b));
-            if (k2 == 0) {
-                for (int l = b; l < 4; ++l) q[l - b] = (uint8_t)(wv[0] >> (8 * l));
-            } else {
-                qw[0] = wv[0];
-            }
-#pragma unroll
-            for (int k = 1; k < 4; ++k) qw[k] = wv[k];
-            if (k2 == 7)
-                for (int l = 0; l < b; ++l) q[16 - b + l] = (uint8_t)(o[3] >> (8 * (4 - b + l)));
-        } else {
-            for (int l = 0; l < nvalid; ++l) q[l] = (uint8_t)(o[l >> 2] >> (8 * (l & 3)));
+        for (int l = 0; l < 4; ++l) {
+            const int c = 4 * bc + l;
+            tile_t[c * 32 + ((rq + 4 * (c >> 4)) & 31)] = col[l];
         }
     }
+    __syncthreads();
+    if (t.local < 0) return;
+    const int T = pow2_exponent(scale);
+    const int64_t H = touts.rows[t.local], W = t.ld;
+    const int64_t hb = (H + kTileDim - 1) / kTileDim, wb = (W + kTileDim - 1) / kTileDim;
+    const int64_t j = t.scale_index % wb, ei = t.scale_index / wb;
+    const int64_t i = ei % hb, e = ei / hb;
+    const int c = threadIdx.x >> 3, k2 = threadIdx.x & 7;
+    const u32x4 vv = *reinterpret_cast<const u32x4*>(&tile_t[c * 32 + ((4 * k2 + 4 * (c >> 4)) & 31)]);
+    const uint32_t v[4] = {vv[0], vv[1], vv[2], vv[3]};
+    wt_row(v, c, k2, T, t, touts.codes[t.local], touts.scale[t.local], H, W, hb, e, i, j);
 }
 
 __global__ __launch_bounds__(kThreads) void encode_kernel(const float* __restrict__ in,
@@ -647,7 +741,8 @@ hipError_t reserve_lds(const void* kernel, std::atomic<uint64_t>& ready) {
     return hipSuccess;
 }
 
-std::atomic<uint64_t> g_step_lds{0}, g_fold_step_lds{0}, g_fold_step_unfold_lds{0};
+std::atomic<uint64_t> g_step_lds{0}, g_fold_step_lds{0}, g_fold_step_unfold_lds{0},
+    g_fold_step_unfold_t_lds{0};
 
 }  // namespace
 
@@ -700,6 +795,20 @@ int launch_unpack(const TileEntry* d_entries, int64_t n_slots, const uint8_t* co
     if (n_slots == 0) return hipSuccess;
     hipLaunchKernelGGL(unpack_kernel, dim3((uint32_t)n_slots), dim3(kThreads), 0,
                        (hipStream_t)stream, d_entries, codes, scale_inv, args);
+    return hipGetLastError();
+}
+
+int launch_fold_step_unfold_t(const TileEntry* d_entries, int64_t n_slots, const PackArgs& grads,
+                              const UnpackArgs& outs, const TransposeArgs& touts, float* master,
+                              float* m, float* v, uint8_t* codes, float* scale_inv,
+                              const StepScalars& s, void* stream) {
+    if (n_slots == 0) return hipSuccess;
+    hipError_t err = reserve_lds(reinterpret_cast<const void*>(fold_step_unfold_t_kernel),
+                                 g_fold_step_unfold_t_lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(fold_step_unfold_t_kernel, dim3((uint32_t)n_slots), dim3(kStepThreads),
+                       kStepLdsBytes, (hipStream_t)stream, d_entries, grads, outs, touts, master, m, v,
+                       reinterpret_cast<uint32_t*>(codes), scale_inv, s, n_slots);
     return hipGetLastError();
 }
 

@@ -215,6 +215,26 @@ int fold_adamw_fp8_step_unpack(const bfz_plan* plan, const float* const* grad, f
                                const bfz_adamw* hp, void* stream);
 
 /*
+ * fold_adamw_fp8_step_unpack with power-of-two scales, plus the transposed
+ * copy of bfz_transpose_pow2, in one pass: the same results, bit for bit, as
+ *     fold_adamw_fp8_step_unpack(plan, grad, master, m, v, codes, scale_inv,
+ *                                dst_fp8, dst_scale, hp, stream);
+ *     bfz_transpose_pow2(plan, codes, scale_inv, dst_t, dst_t_scale, stream);
+ * with W^T built from the step's codes in LDS instead of read back ("FP8-Flow-
+ * MoE", section 3.1: the column-wise copy the backward pass reads, made by
+ * exponent edits only).  hp->scale_pow2 must be set (BFZ_EINVAL otherwise).
+ * dst_t / dst_t_scale: as in bfz_transpose_pow2.  codes and scale_inv may
+ * both be NULL (no tile-major copy).  Other arguments as in
+ * fold_adamw_fp8_step_unpack.
+ * Errors: BFZ_EINVAL, BFZ_EALIGN, BFZ_ESTATE, BFZ_EHIP.
+ */
+int fold_adamw_fp8_step_unpack_t(const bfz_plan* plan, const float* const* grad, float* master,
+                                 float* m, float* v, uint8_t* codes, float* scale_inv,
+                                 uint8_t* const* dst_fp8, float* const* dst_scale,
+                                 uint8_t* const* dst_t, float* const* dst_t_scale,
+                                 const bfz_adamw* hp, void* stream);
+
+/*
  * Unfold of the rank's owned slots: dst_fp8[p][e][128 i + a][128 j + b] =
  * codes[s][a][b] inside the weight's edge, and dst_scale[p][(e hb + i) wb + j]
  * = scale_inv[s] (hb = ceil(H/128), wb = ceil(W/128): the row-major scale

@@ -23,13 +23,17 @@ class GpuWorkload:
 
     MODES = ("unfused", "fused", "fused_unpack")
 
-    def __init__(self, w: WL.Workload, device="cuda", mode="unfused", pow2=False):
+    def __init__(self, w: WL.Workload, device="cuda", mode="unfused", pow2=False, transposed=False):
         """mode: how a step is taken --
         "unfused": pack_shard + adamw_fp8_step (then unpack_fp8 on demand);
         "fused": fold_adamw_fp8_step (gradients read row-major);
         "fused_unpack": fold_adamw_fp8_step_unpack, which also writes the
-        row-major FP8 weights and scale grids (self.out_fp8 / self.out_scale)."""
+        row-major FP8 weights and scale grids (self.out_fp8 / self.out_scale).
+        transposed (fused_unpack with pow2 only): fold_adamw_fp8_step_unpack_t,
+        which also writes W^T and its group scales (self.out_t / self.out_t_scale)."""
         assert mode in self.MODES, mode
+        assert not transposed or (mode == "fused_unpack" and pow2), "transposed: fused_unpack + pow2"
+        self.transposed = transposed
         self.w = w
         self.mode = mode
         self.pow2 = pow2  # power-of-two tile scales
@@ -56,8 +60,11 @@ class GpuWorkload:
         self.tile_codes = True
         self.t_done = 0
         self.out_fp8 = self.out_scale = None
+        self.out_t = self.out_t_scale = None
         if mode == "fused_unpack":
             self.out_fp8, self.out_scale = self.alloc_rowmajor_out()
+        if transposed:
+            self.out_t, self.out_t_scale = self.alloc_transposed_out()
 
     # ---- inputs ------------------------------------------------------------
     def _rowmajor(self, tensor, step=0):
@@ -96,6 +103,12 @@ class GpuWorkload:
 
     def fold_step_unpack(self, t):
         codes, scale = (self.codes, self.scale_inv) if self.tile_codes else (None, None)
+        if self.transposed:
+            bfz.fold_adamw_fp8_step_unpack_t(self.plan, self.grad_rm, self.master, self.m, self.v,
+                                             codes, scale, self.out_fp8, self.out_scale,
+                                             self.out_t, self.out_t_scale,
+                                             hp_for(self.w, t, self.pow2))
+            return
         bfz.fold_adamw_fp8_step_unpack(self.plan, self.grad_rm, self.master, self.m, self.v,
                                        codes, scale, self.out_fp8, self.out_scale,
                                        hp_for(self.w, t, self.pow2))
@@ -136,6 +149,15 @@ class GpuWorkload:
             sc[p] = torch.zeros(E * (-(-H // 128)) * (-(-W // 128)), dtype=torch.float32,
                                 device=self.device)
         return fp8, sc
+
+    def alloc_transposed_out(self):
+        wt = [None] * len(self.w.dims)
+        wts = [None] * len(self.w.dims)
+        for p in self.touched:
+            E, H, W = self.w.dims[p]
+            wt[p] = torch.zeros(E * W * H, dtype=torch.uint8, device=self.device)
+            wts[p] = torch.zeros(E * W * (-(-H // 128)), dtype=torch.float32, device=self.device)
+        return wt, wts
 
     def unpack(self, fp8, sc):
         bfz.unpack_fp8(self.plan, self.codes, self.scale_inv, fp8, sc)

@@ -180,6 +180,34 @@ int launch_fold_step_unfold(const TileEntry* e, int64_t n, const PackArgs& grads
     return 0;
 }
 
+int launch_fold_step_unfold_t(const TileEntry* e, int64_t n, const PackArgs& grads,
+                              const UnpackArgs& outs, const TransposeArgs& touts, float* master,
+                              float* m, float* v, uint8_t* codes, float* scale_inv,
+                              const StepScalars& s, void* stream) {
+    // the step and row-major output as launch_fold_step_unfold (which records
+    // the segment), then the transposed placement from the tile's codes
+    // (low bytes of the updated master)
+    if (int err = launch_fold_step_unfold(e, n, grads, outs, master, m, v, codes, scale_inv, s, stream))
+        return err;
+    for (int64_t sl = 0; sl < n; ++sl) {
+        const TileEntry& t = e[sl];
+        if (t.local < 0) continue;
+        const int64_t H = touts.rows[t.local], W = t.ld;
+        const int64_t hb = (H + kTileDim - 1) / kTileDim, wb = (W + kTileDim - 1) / kTileDim;
+        const int64_t j = t.scale_index % wb, ei = t.scale_index / wb, i = ei % hb, ex = ei / hb;
+        for (int c = 0; c < t.valid_cols; ++c) {
+            const int64_t out_row = ex * W + kTileDim * j + c;
+            for (int r = 0; r < t.valid_rows; ++r) {
+                uint32_t bits;
+                std::memcpy(&bits, &master[sl * kTileElems + r * kTileDim + c], 4);
+                touts.codes[t.local][out_row * H + kTileDim * i + r] = uint8_t(bits);
+            }
+            touts.scale[t.local][out_row * hb + i] = 1.0f;
+        }
+    }
+    return 0;
+}
+
 int launch_transpose_pow2(const TileEntry* e, int64_t n, const uint8_t* codes,
                           const float* scale_inv, const TransposeArgs& args, void*) {
     if (int err = record(e, n)) return err;
@@ -400,6 +428,18 @@ void run_plan_case(const std::vector<int64_t>& dims, int32_t D) {
                                          nullptr, w8.data(), grid.data(), &hp, nullptr) == BFZ_OK,
               "one-kernel step without tile-major codes: %s", bfz_last_error());
         check_segments(plan, q, false, "fold_adamw_fp8_step_unpack (row-major only)");
+        bfz_adamw hp2 = hp;
+        CHECK(fold_adamw_fp8_step_unpack_t(plan, const_cast<const float* const*>(grads.data()), shard, m, v,
+                                           codes, sc, w8.data(), grid.data(), wt8.data(), tgrid.data(), &hp2,
+                                           nullptr) == BFZ_EINVAL,
+              "transposed copy without power-of-two scales");
+        g_calls.clear();
+        hp2.scale_pow2 = 1;
+        CHECK(fold_adamw_fp8_step_unpack_t(plan, const_cast<const float* const*>(grads.data()), shard, m, v,
+                                           codes, sc, w8.data(), grid.data(), wt8.data(), tgrid.data(), &hp2,
+                                           nullptr) == BFZ_OK,
+              "one-kernel step with the transposed copy: %s", bfz_last_error());
+        check_segments(plan, q, false, "fold_adamw_fp8_step_unpack_t");
 
         // a launch failure surfaces as BFZ_EHIP with a message
         if (q > 0) {

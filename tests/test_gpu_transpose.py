@@ -12,7 +12,7 @@ import oracle
 from synth import workloads as WL
 from tests.compare import compare
 from tests.gpu_run import GpuWorkload
-from tests.oracle_run import oracle_slots
+from tests.oracle_run import oracle_slots, sample_slots
 
 pytestmark = pytest.mark.gpu
 
@@ -126,3 +126,89 @@ def test_transpose_quantized_weights():
     for p in range(len(dims)):
         assert np.array_equal(dt[p].cpu().numpy(), odt[p].reshape(-1)), p
         assert np.array_equal(ds[p].cpu().numpy(), ods[p].reshape(-1)), p
+
+
+@pytest.mark.parametrize("tile_codes", [True, False])
+def test_fused_step_with_transposed_copy(tile_codes):
+    """fold_adamw_fp8_step_unpack_t over the steps of ten ragged matrices:
+    master, moments, codes and scales, the row-major FP8 weights and the
+    transposed copy all equal the oracle's power-of-two step followed by its
+    unfold and its transposed copy, bit for bit (without the tile-major copy
+    when tile_codes is False: those buffers stay untouched)."""
+    w = WL.ragged()
+    w.dims = w.dims[:10]
+    _say("fused step + transposed copy: 10 ragged matrices, D=8 rank 3, tile codes", tile_codes)
+    g = GpuWorkload(w, mode="fused_unpack", pow2=True, transposed=True)
+    g.tile_codes = tile_codes
+    g.codes.fill_(0xAB)
+    g.scale_inv.fill_(-7.0)
+    g.load_state()
+    g.run_steps()
+    slots = list(range(g.q))
+    ora = oracle_slots(w, slots, pow2=True)
+    got = g.tiles(slots)
+    for name in ("master", "m", "v"):
+        assert np.array_equal(got[name].view(np.uint32), ora[name].view(np.uint32)), name
+    if tile_codes:
+        assert np.array_equal(got["codes"], ora["codes"]) and np.array_equal(got["scale_inv"], ora["scale_inv"])
+    else:
+        assert (got["codes"] == 0xAB).all() and (got["scale_inv"] == -7.0).all()
+    q, owned, table = oracle.plan(w.dims, w.D, w.rank)
+    o8 = [np.zeros((E, H, W), np.uint8) for E, H, W in w.dims]
+    osc = [np.zeros((E, -(-H // 128), -(-W // 128)), np.float32) for E, H, W in w.dims]
+    oracle.unpack(w.dims, ora["codes"].reshape(-1), ora["scale_inv"], table, o8, osc)
+    odt, ods = _oracle_outputs(w.dims)
+    oracle.transpose_pow2(w.dims, ora["codes"].reshape(-1), ora["scale_inv"], table, odt, ods)
+    torch.cuda.synchronize()
+    for p in g.touched:
+        E, H, W = w.dims[p]
+        rows = table[:owned][table[:owned, 0] == p]
+        # only the rank's own tiles are written: compare those blocks
+        fp8 = g.out_fp8[p].view(E, H, W).cpu().numpy()
+        wt = g.out_t[p].view(E, W, H).cpu().numpy()
+        wts = g.out_t_scale[p].view(E, W, -(-H // 128)).cpu().numpy()
+        sc = g.out_scale[p].view(E, -(-H // 128), -(-W // 128)).cpu().numpy()
+        for _, e, i, j, vr, vc in rows:
+            assert np.array_equal(fp8[e, 128 * i:128 * i + vr, 128 * j:128 * j + vc],
+                                  o8[p][e, 128 * i:128 * i + vr, 128 * j:128 * j + vc]), (p, e, i, j)
+            assert sc[e, i, j] == osc[p][e, i, j]
+            assert np.array_equal(wt[e, 128 * j:128 * j + vc, 128 * i:128 * i + vr],
+                                  odt[p][e, 128 * j:128 * j + vc, 128 * i:128 * i + vr]), (p, e, i, j)
+            assert np.array_equal(wts[e, 128 * j:128 * j + vc, i], ods[p][e, 128 * j:128 * j + vc, i])
+    del g
+
+
+def test_fused_transposed_copy_full_size_sampled():
+    """The dense-LLM shard (all 11 steps) through fold_adamw_fp8_step_unpack_t,
+    as bench.py --path fused_unpack_t times it: sampled tiles against the
+    oracle -- state, codes, scales, row-major FP8 and the W^T block with its
+    group scales (the oracle's transposed copy of that tile alone)."""
+    w = WL.dense_llm()
+    _say("dense_llm full size, fused step + transposed copy, pow2")
+    g = GpuWorkload(w, mode="fused_unpack", pow2=True, transposed=True)
+    g.load_state()
+    g.run_steps()
+    slots = sample_slots(w, n_random=48)
+    ora = oracle_slots(w, slots, pow2=True)
+    rep = compare(g.tiles(slots), ora)
+    _say({k: v for k, v in rep.items() if k != "fail"})
+    assert rep["ok"] and rep["exact"], rep["fail"]
+    torch.cuda.synchronize()
+    for k, s in enumerate(slots):
+        p, e, i, j, vr, vc = (int(x) for x in ora["table"][k])
+        if p < 0:
+            continue
+        E, H, W = w.dims[p]
+        hb = -(-H // 128)
+        block = g.out_fp8[p].view(E, H, W)[e, 128 * i:128 * i + vr, 128 * j:128 * j + vc]
+        assert np.array_equal(block.cpu().numpy(), ora["codes"][k].reshape(128, 128)[:vr, :vc]), s
+        one_dt = [np.zeros((1, vc, vr), np.uint8)]
+        one_ds = [np.zeros((1, vc, 1), np.float32)]
+        oracle.transpose_pow2([(1, vr, vc)], np.ascontiguousarray(ora["codes"][k].reshape(-1)),
+                              np.array([ora["scale_inv"][k]], np.float32),
+                              np.array([[0, 0, 0, 0, vr, vc]], np.int64), one_dt, one_ds)
+        wt = g.out_t[p].view(E, W, H)[e, 128 * j:128 * j + vc, 128 * i:128 * i + vr]
+        wts = g.out_t_scale[p].view(E, W, hb)[e, 128 * j:128 * j + vc, i]
+        assert np.array_equal(wt.cpu().numpy(), one_dt[0][0]), s
+        assert np.array_equal(wts.cpu().numpy(), one_ds[0][0, :, 0]), s
+    del g
