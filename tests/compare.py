@@ -24,7 +24,7 @@ def _dec():
 
 
 def compare(gpu: dict, ora: dict):
-    """Returns a report dict; report['ok'] is the spec verdict."""
+    """Returns a report dict; report['ok'] says whether every element meets the bar above."""
     rep = {"ok": True, "fail": []}
     for k in ("master", "m", "v"):
         g = np.asarray(gpu[k], dtype=np.float64).reshape(-1)
