@@ -470,36 +470,50 @@ __device__ __forceinline__ float pow2_value(int T) {
     return T >= -126 ? __uint_as_float((uint32_t)(T + 127) << 23) : __uint_as_float(1u << (T + 149));
 }
 
-// Largest E4M3 magnitude (low 7 bits) among the 16 codes of four words.
-__device__ __forceinline__ uint32_t mag_max16(const uint32_t v[4]) {
-    uint32_t m = 0;
+// Largest of the 16 bytes of four words whose bytes are below 0x80 (E4M3
+// magnitudes with the sign masked off).
+__device__ __forceinline__ uint32_t byte_max16(const uint32_t a[4]) {
+    uint32_t m[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t a = max(__builtin_amdgcn_ubfe(v[q], 0, 7), __builtin_amdgcn_ubfe(v[q], 8, 7));
-        const uint32_t b = max(__builtin_amdgcn_ubfe(v[q], 16, 7), __builtin_amdgcn_ubfe(v[q], 24, 7));
-        m = max(m, max(a, b));
-    }
-    return m;
+    for (int q = 0; q < 4; ++q)
+        m[q] = max(max(a[q] & 0xFFu, (a[q] >> 8) & 0xFFu), max((a[q] >> 16) & 0xFFu, a[q] >> 24));
+    return max(max(m[0], m[1]), max(m[2], m[3]));
+}
+
+// The 8-entry byte table c -> e4m3_scale_up(c, d) for the subnormal codes
+// c = 0..7, d = 0..17, as two words (entries 0-3 in lo, 4-7 in hi).  A code
+// c takes s = 4 - bitlength(c) doublings as a left shift (3 for c = 1, 2 for
+// c = 2, 3, 1 for c = 4..7) and the rest as +8 each; no entry exceeds 142,
+// so the per-byte sums never carry.
+__device__ __forceinline__ void subnormal_table(int d, uint32_t& lo, uint32_t& hi) {
+    hi = d >= 1 ? 0x0E0C0A08u + (uint32_t)(d - 1) * 0x08080808u : 0x07060504u;
+    lo = d >= 2 ? 0x0C080000u + (uint32_t)(d - 2) * 0x08080800u : (d == 1 ? 0x06040200u : 0x03020100u);
+    if (d == 2) lo |= 0x0400u;  // c = 1 is still subnormal after two doublings
 }
 
 // One lane's part of W^T row c of a tile: the lane holds bytes 16 k2 .. +15
 // of the row (tile rows 16 k2 .. +15 of column c) in v, 8 lanes per row.
 // The group's largest magnitude code (valid rows only; an 8-lane shuffle
 // reduction) gives the headroom d (clamped so 2^(T - d) >= 2^-149), lane 0
-// writes the group scale, and every code is moved up d binades: one add per
-// 32-bit word when the lane's codes are all normal or zero (8d on each
-// normal byte cannot carry out of it: the headroom keeps every code <= 126),
-// byte by byte when one is subnormal or on a ragged edge.  All 8 lanes of
-// the row must call it (shuffles).  An all-zero group: scale 1, codes 0.
+// writes the group scale, and every code is moved up d binades.  A normal
+// code moves by adding 8d to its byte -- one add per 32-bit word, which
+// cannot carry out of a byte since the headroom keeps every code <= 126;
+// subnormal codes (rare: magnitudes under 2^-6 of the scale) are looked up,
+// four bytes at a time, in a byte table indexed by their 3-bit value; a
+// lane on a ragged edge goes byte by byte.  All 8 lanes of the row must
+// call it (shuffles).  An all-zero group: scale 1, codes 0.
 __device__ __forceinline__ void wt_row(const uint32_t v[4], int c, int k2, int T, const TileEntry& t,
                                        uint8_t* wt, float* wt_scale, int64_t H, int64_t W,
                                        int64_t hb, int64_t e, int64_t i, int64_t j) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const int r0 = 16 * k2;
     const int nvalid = max(0, min(16, (int)t.valid_rows - r0));
+    uint32_t a[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a[q] = v[q] & 0x7F7F7F7Fu;
     uint32_t mx = 0;
     if (nvalid == 16) {
-        mx = mag_max16(v);
+        mx = byte_max16(a);
     } else {
         for (int l = 0; l < nvalid; ++l) mx = max(mx, (v[l >> 2] >> (8 * (l & 3))) & 0x7Fu);
     }
@@ -513,25 +527,30 @@ __device__ __forceinline__ void wt_row(const uint32_t v[4], int c, int k2, int T
     if (k2 == 0) wt_scale[out_row * hb + i] = mx == 0u ? 1.0f : pow2_value(T - d);
     if (nvalid == 0) return;
     uint32_t o[4] = {0u, 0u, 0u, 0u};
-    if (mx != 0u) {
-        // per byte: bit 7 of nf set for a normal code (exponent field != 0);
-        // sub collects nonzero codes that are not normal
-        uint32_t nf[4], sub = 0;
+    if (mx != 0u && nvalid == 16) {
+        // per byte: bit 7 of nf set for a normal code (exponent field != 0),
+        // bit 7 of sub for a nonzero code that is not normal
+        uint32_t nf[4], sub[4];
+        const uint32_t inc = (uint32_t)d << 3;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const uint32_t a = v[q] & 0x7F7F7F7Fu;
-            nf[q] = ((a & 0x78787878u) + 0x78787878u) & 0x80808080u;
-            sub |= ((a + 0x7F7F7F7Fu) & 0x80808080u) & ~nf[q];
+            nf[q] = ((a[q] & 0x78787878u) + 0x78787878u) & 0x80808080u;
+            sub[q] = ((a[q] + 0x7F7F7F7Fu) & 0x80808080u) & ~nf[q];
+            o[q] = v[q] + (nf[q] >> 7) * inc;
         }
-        if (nvalid == 16 && sub == 0u) {
-            const uint32_t inc = (uint32_t)d << 3;
+        if ((sub[0] | sub[1] | sub[2] | sub[3]) != 0u) {
+            uint32_t lo, hi;
+            subnormal_table(d, lo, hi);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] = v[q] + (nf[q] >> 7) * inc;
-        } else {
-            for (int l = 0; l < 16; ++l)
-                o[l >> 2] |= (l < nvalid ? e4m3_scale_up((v[l >> 2] >> (8 * (l & 3))) & 0xFFu, d) : 0u)
-                             << (8 * (l & 3));
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t looked = __builtin_amdgcn_perm(hi, lo, v[q] & 0x07070707u) | (v[q] & 0x80808080u);
+                const uint32_t bytes = sub[q] | (sub[q] - (sub[q] >> 7));  // 0xFF where sub
+                o[q] = (looked & bytes) | (o[q] & ~bytes);
+            }
         }
+    } else if (mx != 0u) {
+        for (int l = 0; l < nvalid; ++l)
+            o[l >> 2] |= e4m3_scale_up((v[l >> 2] >> (8 * (l & 3))) & 0xFFu, d) << (8 * (l & 3));
     }
     uint8_t* q = wt + out_row * H + kTileDim * i + r0;
     // The row's 128-byte segment starts b bytes past a 4-byte boundary
