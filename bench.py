@@ -49,7 +49,7 @@ UNPACK_BYTES_PER_ELEM = 2         # read code + write code
 UNPACK_BYTES_PER_TILE = 8         # read + write scale
 TRAFFIC_FILES = {k: os.path.join(ROOT, "profiles", f"{k}_dense_llm_traffic.md")
                  for k in ("fold_step_unfold_kernel", "fold_step_kernel", "step_kernel",
-                           "transpose_pow2_kernel")}
+                           "transpose_pow2_kernel", "fold_step_unfold_t_kernel")}
 KERNEL_OF_PATH = {"fused_unpack": "fold_step_unfold_kernel",
                   "fused_unpack_t": "fold_step_unfold_t_kernel", "fused": "fold_step_kernel",
                   "unfused": "step_kernel"}
