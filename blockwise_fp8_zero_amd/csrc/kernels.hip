@@ -355,7 +355,8 @@ __global__ __launch_bounds__(kStepThreads) void pack_kernel(const TileEntry* __r
     for (int k = 0; k < kStepVec; ++k) store_stream(out + k * kStepThreads + threadIdx.x, x[k]);
 }
 
-// Unfold of codes and scales: one workgroup per owned slot.  Thread t moves
+// Unfold of codes and scales: one workgroup per owned slot, XCD-contiguous
+// (measured 5.6% faster than plain order on the dense shard).  Thread t moves
 // 16 codes (column block t % 8) of rows t / 8, t / 8 + 32, ...  A row of a
 // full-width tile goes out as one 16-byte store per lane when it starts on a
 // 16-byte boundary, as 4-byte words when on a 4-byte boundary, and otherwise
@@ -370,7 +371,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const TileEntry* __res
                                                           const float* __restrict__ scale_inv,
                                                           UnpackArgs args) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const int64_t slot = blockIdx.x;
+    const int64_t slot = xcd_tile(blockIdx.x, gridDim.x);
     const TileEntry t = entries[slot];
     if (t.local < 0) return;
     const u32x4* in = reinterpret_cast<const u32x4*>(codes + slot * kTileElems);
@@ -607,6 +608,9 @@ __global__ __launch_bounds__(kThreads) void transpose_pow2_kernel(
     const float* __restrict__ scale_inv, TransposeArgs args) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     __shared__ uint32_t tile_t[kTileDim * 32];
+    // Plain order (workgroup b on XCD b % 8), measured 1.5-7% faster here
+    // than XCD-contiguous ranges (likely because each XCD's tiles in flight
+    // then span more tile rows of the same tile columns: longer W^T row runs).
     const int64_t slot = blockIdx.x;
     const TileEntry t = entries[slot];
     if (t.local < 0) return;
