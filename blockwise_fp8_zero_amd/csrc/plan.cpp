@@ -15,6 +15,7 @@
 
 #include <algorithm>
 #include <limits>
+#include <memory>
 #include <new>
 
 #include "bfz_internal.h"
@@ -22,6 +23,11 @@
 namespace {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The plan's tables, once the arguments are known to be valid (may throw
+// std::bad_alloc, which bfz_plan_create turns into an error code).
+int build_plan(const int64_t* dims, int32_t n_weights, int32_t D, int32_t rank, int64_t total,
+               bfz_plan** out);
 
 }  // namespace
 
@@ -47,9 +53,24 @@ extern "C" int bfz_plan_create(const int64_t* dims, int32_t n_weights, int32_t D
             return fail(BFZ_EINVAL, "bfz_plan_create: weight %d has more than 2^31 - 1 tiles", p);
         total += E * grid;
     }
+    // A shard beyond 2^31 - 1 tiles (3.5e13 elements) is far past any one
+    // GPU's memory; refusing it keeps the host table (76 B per slot) sane.
+    if (ceil_div(total, D) > int64_t(INT32_MAX))
+        return fail(BFZ_EINVAL, "bfz_plan_create: %lld tiles over %d ranks is more than 2^31 - 1 per rank",
+                    (long long)total, D);
+    try {
+        return build_plan(dims, n_weights, D, rank, total, out);
+    } catch (const std::bad_alloc&) {
+        return fail(BFZ_EINVAL, "bfz_plan_create: out of host memory");
+    }
+}
 
-    bfz_plan* plan = new (std::nothrow) bfz_plan;
-    if (!plan) return fail(BFZ_EINVAL, "bfz_plan_create: out of host memory");
+namespace {
+
+int build_plan(const int64_t* dims, int32_t n_weights, int32_t D, int32_t rank, int64_t total,
+               bfz_plan** out) {
+    using namespace bfz;
+    std::unique_ptr<bfz_plan> plan(new bfz_plan);
     plan->n_weights = n_weights;
     plan->D = D;
     plan->rank = rank;
@@ -110,9 +131,11 @@ extern "C" int bfz_plan_create(const int64_t* dims, int32_t n_weights, int32_t D
     if (plan->owned < q) {  // padding slots ride in a segment of their own
         plan->segments.push_back(Segment{plan->owned, q - plan->owned, 0, 0});
     }
-    *out = plan;
+    *out = plan.release();
     return BFZ_OK;
 }
+
+}  // namespace
 
 // "Param-wise split" (the alternative the page rejects, kept to compare
 // padding): weights sorted by size, largest first, each dealt to the bucket
@@ -126,13 +149,23 @@ extern "C" int bfz_paramwise_split(const int64_t* dims, int32_t n_weights, int32
         return fail(BFZ_EINVAL, "bfz_paramwise_split: null pointer");
     if (n_weights < 1 || D < 1)
         return fail(BFZ_EINVAL, "bfz_paramwise_split: need n_params >= 1 and D >= 1");
-    std::vector<std::pair<int64_t, int32_t>> order(n_weights);
+    std::vector<std::pair<int64_t, int32_t>> order;
+    try {
+        order.resize(n_weights);
+    } catch (const std::bad_alloc&) {
+        return fail(BFZ_EINVAL, "bfz_paramwise_split: out of host memory");
+    }
+    // every bucket's sum stays below 2^62 when the total does
+    int64_t total = 0;
     for (int32_t p = 0; p < n_weights; ++p) {
         const int64_t E = dims[3 * p], H = dims[3 * p + 1], W = dims[3 * p + 2];
         if (E < 1 || H < 1 || W < 1 || H > (int64_t(1) << 31) || W > (int64_t(1) << 31) ||
             E > (int64_t(1) << 62) / (H * W))
             return fail(BFZ_EINVAL, "bfz_paramwise_split: weight %d has bad dims", p);
         order[p] = {E * H * W, p};
+        if (order[p].first > (int64_t(1) << 62) - total)
+            return fail(BFZ_EINVAL, "bfz_paramwise_split: more than 2^62 elements in all");
+        total += order[p].first;
     }
     std::stable_sort(order.begin(), order.end(),
                      [](const auto& a, const auto& b) { return a.first > b.first; });

@@ -83,7 +83,9 @@ typedef struct {
  * how the page deals tiles to ranks).  Host only: touches no GPU.
  * On success *out receives a new plan.  Errors: BFZ_EINVAL for null
  * pointers, n_params < 1, D < 1, rank outside [0, D), a dimension < 1,
- * H, W > 2^31 - 1, or a weight of more than 2^31 - 1 tiles.
+ * H, W > 2^31 - 1, a weight of more than 2^31 - 1 tiles, a quota q of more
+ * than 2^31 - 1 tiles, or too little host memory for the table (76 bytes
+ * per slot).
  */
 int bfz_plan_create(const int64_t* dims, int32_t n_params, int32_t D, int32_t rank,
                     bfz_plan** out);
@@ -122,7 +124,8 @@ int bfz_plan_tile(const bfz_plan* plan, int64_t slot, int64_t out[6]);
  * every bucket is then padded to the largest.  Host only.
  * dims as in bfz_plan_create.  Out: bucket_of_param[n_params] in [0, D),
  * bucket_elems[D] the elements per bucket (padded shard = their maximum).
- * Errors: BFZ_EINVAL.
+ * Errors: BFZ_EINVAL (null pointers, n_params < 1, D < 1, a dimension < 1,
+ * H, W > 2^31, more than 2^62 elements in all, too little host memory).
  */
 int bfz_paramwise_split(const int64_t* dims, int32_t n_params, int32_t D,
                         int32_t* bucket_of_param, int64_t* bucket_elems);

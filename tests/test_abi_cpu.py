@@ -71,12 +71,20 @@ def test_paramwise_split_matches_oracle():
         bfz.paramwise_split([(1, 0, 3)], 2)
     with pytest.raises(bfz.BfzError):
         bfz.paramwise_split([(1, 2, 3)], 0)
+    # each weight is within bounds, their sum (2^63 elements) is not
+    with pytest.raises(bfz.BfzError):
+        bfz.paramwise_split([(1, 2 ** 31, 2 ** 31)] * 2, 2)
+    bop, be = bfz.paramwise_split([(1, 2 ** 31, 2 ** 30)] * 2, 2)
+    assert list(be) == [2 ** 61, 2 ** 61]
 
 
 @pytest.mark.parametrize("dims,D,rank", [
     ([(1, 10, 10)], 0, 0), ([(1, 10, 10)], 2, 2), ([(1, 10, 10)], 2, -1),
     ([(0, 10, 10)], 1, 0), ([(1, 10, -3)], 1, 0), ([(1, 2 ** 31, 5)], 1, 0), ([], 1, 0),
     ([(2 ** 20, 8192, 8192)], 4096, 0),  # 2^32 tiles: the scale-grid index would overflow
+    # three weights of 2^31 - 4096 tiles each: a quota past 2^31 - 1 tiles per rank,
+    # refused before any table is allocated
+    ([(2 ** 19 - 1, 8192, 8192)] * 3, 1, 0), ([(2 ** 19 - 1, 8192, 8192)] * 3, 2, 1),
 ])
 def test_plan_rejects_bad_arguments(dims, D, rank):
     with pytest.raises(bfz.BfzError) as e:
