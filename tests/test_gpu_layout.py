@@ -23,7 +23,7 @@ CASES = [
     ([(1, 129, 300), (2, 200, 257), (1, 1, 1), (3, 128, 128)], 3, 1),
     ([(2, 383, 130), (1, 77, 1029), (1, 640, 16)], 4, 3),
     ([(1, 200, 130)], 3, 2),            # more ranks than tiles: rank 2 owns nothing
-    ([(1, 130, 131)] * 70, 2, 0),       # > 64 weights: several launch segments
+    ([(1, 130, 131)] * 140, 2, 1),      # rank owns 70 weights: several launch segments
 ]
 
 

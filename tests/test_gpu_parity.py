@@ -332,6 +332,82 @@ def test_random_configurations(seed):
                 assert np.array_equal(dsc[k].cpu().numpy(), osc[k].reshape(-1)), k
 
 
+@pytest.mark.parametrize("pow2", [False, True])
+def test_many_weights_several_segments(pow2):
+    """A rank that owns 70+ small ragged weights, starting and ending
+    mid-weight: its slots span several launch segments (at most 64 weights
+    each) in every route -- tile-major step, fused fold, one-kernel step
+    and, with power-of-two scales, the step that also writes W^T -- each
+    checked on every slot and every row-major output against the oracle."""
+    rng = np.random.default_rng(2000 + int(pow2))
+    dims = [(int(rng.integers(1, 3)), int(rng.integers(1, 260)), int(rng.integers(1, 260)))
+            for _ in range(250)]
+    D, rank = 3, 1
+    q, owned, table = oracle.plan(dims, D, rank)
+    touched = sorted(set(int(p) for p in table[:owned, 0]))
+    assert len(touched) > 64 and owned > 0
+    assert tuple(table[0][1:4]) != (0, 0, 0)                         # starts inside a weight
+    assert oracle.plan(dims, D, rank + 1)[2][0][0] == table[owned - 1][0]  # ends inside one
+    _say("many weights: 250 ragged, D", D, "rank", rank, "owns", owned, "tiles of", len(touched),
+         "weights, pow2", pow2)
+    host = {k: [rng.normal(0, s, d).astype(np.float32) for d in dims]
+            for k, s in (("p", 0.02), ("g", 1e-3), ("m", 1e-4))}
+    host["v"] = [np.square(rng.normal(0, 1e-3, d)).astype(np.float32) for d in dims]
+    ora = {k: oracle.pack(dims, host[k], table) for k in ("p", "g", "m", "v")}
+    hp = dict(lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+    codes_o, scale_o, near_o = oracle.step(ora["p"], ora["g"], ora["m"], ora["v"],
+                                           oracle.hparams(step=3, **hp), pow2=pow2)
+    o8 = [np.zeros(d, dtype=np.uint8) for d in dims]
+    osc = [np.zeros((d[0], -(-d[1] // 128), -(-d[2] // 128)), dtype=np.float32) for d in dims]
+    oracle.unpack(dims, codes_o, scale_o, table, o8, osc)
+    if pow2:
+        ot = [np.zeros((d[0], d[2], d[1]), dtype=np.uint8) for d in dims]
+        ots = [np.zeros((d[0], d[2], -(-d[1] // 128)), dtype=np.float32) for d in dims]
+        oracle.transpose_pow2(dims, codes_o, scale_o, table, ot, ots)
+    plan = bfz.Plan(dims, D, rank)
+    dev = {k: [torch.from_numpy(x.reshape(-1)).cuda() for x in host[k]] for k in host}
+    routes = ["unfused", "fused", "fused_unpack"] + (["fused_unpack_t"] if pow2 else [])
+    for route in routes:
+        st = {}
+        for k in ("p", "m", "v"):
+            st[k] = torch.empty(q * 16384, dtype=torch.float32, device="cuda")
+            bfz.pack_shard(plan, dev[k], st[k])
+        codes = torch.empty(q * 16384, dtype=torch.uint8, device="cuda")
+        sc = torch.empty(q, dtype=torch.float32, device="cuda")
+        h = bfz.AdamW(step=3, scale_pow2=int(pow2), **hp)
+        d8 = [torch.zeros(int(np.prod(d)), dtype=torch.uint8, device="cuda") for d in dims]
+        dsc = [torch.zeros(osc[k].size, dtype=torch.float32, device="cuda") for k in range(len(dims))]
+        if route == "unfused":
+            gt = torch.empty(q * 16384, dtype=torch.float32, device="cuda")
+            bfz.pack_shard(plan, dev["g"], gt)
+            bfz.adamw_fp8_step(st["p"], gt, st["m"], st["v"], codes, sc, h)
+            bfz.unpack_fp8(plan, codes, sc, d8, dsc)
+        elif route == "fused":
+            bfz.fold_adamw_fp8_step(plan, dev["g"], st["p"], st["m"], st["v"], codes, sc, h)
+            bfz.unpack_fp8(plan, codes, sc, d8, dsc)
+        elif route == "fused_unpack":
+            bfz.fold_adamw_fp8_step_unpack(plan, dev["g"], st["p"], st["m"], st["v"], codes, sc,
+                                           d8, dsc, h)
+        else:
+            dt = [torch.zeros(int(np.prod(d)), dtype=torch.uint8, device="cuda") for d in dims]
+            dts = [torch.zeros(ots[k].size, dtype=torch.float32, device="cuda")
+                   for k in range(len(dims))]
+            bfz.fold_adamw_fp8_step_unpack_t(plan, dev["g"], st["p"], st["m"], st["v"], codes, sc,
+                                             d8, dsc, dt, dts, h)
+        torch.cuda.synchronize()
+        gpu = dict(master=st["p"].cpu().numpy(), m=st["m"].cpu().numpy(), v=st["v"].cpu().numpy(),
+                   codes=codes.cpu().numpy(), scale_inv=sc.cpu().numpy())
+        rep = _check(gpu, dict(master=ora["p"], m=ora["m"], v=ora["v"], codes=codes_o,
+                               scale_inv=scale_o, near=near_o), f"many weights {route}")
+        assert rep["exact"]
+        for k in range(len(dims)):
+            assert np.array_equal(d8[k].cpu().numpy(), o8[k].reshape(-1)), (route, k)
+            assert np.array_equal(dsc[k].cpu().numpy(), osc[k].reshape(-1)), (route, k)
+            if route == "fused_unpack_t":
+                assert np.array_equal(dt[k].cpu().numpy(), ot[k].reshape(-1)), (route, k)
+                assert np.array_equal(dts[k].cpu().numpy(), ots[k].reshape(-1)), (route, k)
+
+
 def test_amax_at_every_position():
     """16384 tiles; tile k has its largest |value| at element k (sign
     alternating).  lr = 0 leaves the master unchanged, so the scale must be

@@ -39,7 +39,7 @@ CASES = [
     ([(1, 256, 384)], 1, 0),
     ([(2, 300, 129), (1, 77, 513), (1, 1, 1)], 1, 0),
     ([(3, 129, 130), (1, 128, 1000)], 3, 1),
-    ([(1, 640, 48)] * 70, 2, 1),   # > 64 weights: several launch segments
+    ([(1, 640, 48)] * 140, 2, 1),  # rank owns 70 weights: several launch segments
 ]
 
 
