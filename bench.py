@@ -12,6 +12,11 @@ grid.  --path picks how:
   fused:   fold_adamw_fp8_step, then unpack_fp8;
   unfused: pack_shard, adamw_fp8_step, unpack_fp8.
 The split itself (the planner) runs once at set-up.
+--layout picks how the FP32 state (master, m, v) sits in HBM:
+  interleaved (default): one contiguous [master | m | v] block per tile
+      (state_stride 49152), so each tile's updated state leaves as one
+      write stream;
+  separate: three tile-major arrays.
 
 Default workload: the dense-LLM rank shard -- 32 layers x {4 of 4096x4096,
 2 of 4096x11008, 1 of 11008x4096}, D = 8, rank 0: 49408 tiles, 809.5M
@@ -236,6 +241,8 @@ def main():
                     help="power-of-two tile scales in the timed steps (bfz_adamw.scale_pow2)")
     ap.add_argument("--skip-transpose", action="store_true",
                     help="do not time bfz_transpose_pow2 after the steps")
+    ap.add_argument("--layout", default="interleaved", choices=["interleaved", "separate"],
+                    help="FP32 state layout (see the module docstring)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
@@ -257,7 +264,7 @@ def main():
     transposed = args.path == "fused_unpack_t"
     one_kernel = args.path in ("fused_unpack", "fused_unpack_t")
     g = GpuWorkload(w, mode="fused_unpack" if one_kernel else args.path,
-                    pow2=args.pow2 or transposed, transposed=transposed)
+                    pow2=args.pow2 or transposed, transposed=transposed, layout=args.layout)
     # a lone rank (D = 1) gathers nothing: its one-kernel step writes only
     # the row-major FP8 weights and scale grids, not the tile-major copy
     lone = one_kernel and w.D == 1
@@ -364,6 +371,9 @@ def main():
             "D": w.D,
             "rank": w.rank,
             "first_timed_step_t": w.measured_step + args.warmup,
+            "state_layout": {"interleaved": "one [master | m | v] block per tile "
+                                            "(state_stride 49152)",
+                             "separate": "three tile-major arrays"}[args.layout],
             "step_path": {"unfused": "pack_shard(grad) + adamw_fp8_step + unpack_fp8",
                           "fused": "fold_adamw_fp8_step + unpack_fp8",
                           "fused_unpack": "fold_adamw_fp8_step_unpack",

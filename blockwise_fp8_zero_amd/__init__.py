@@ -26,10 +26,12 @@ class BfzError(RuntimeError):
 
 class AdamW(C.Structure):
     """Hyper-parameters of one step; step is the counter t >= 1; scale_pow2
-    selects power-of-two tile scales."""
+    selects power-of-two tile scales; state_stride (floats between tiles of
+    master / m / v) is filled in by the step functions from the state
+    tensors' layout -- leave it 0."""
     _fields_ = [("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
                 ("eps", C.c_double), ("weight_decay", C.c_double), ("step", C.c_int64),
-                ("scale_pow2", C.c_int32)]
+                ("scale_pow2", C.c_int32), ("state_stride", C.c_int64)]
 
 
 _lib = None
@@ -55,6 +57,7 @@ def lib():
         L.bfz_plan_tile.argtypes = [P, i64, P]
         L.bfz_paramwise_split.argtypes = [P, i32, i32, P, P]
         L.pack_shard.argtypes = [P, P, P, P]
+        L.pack_shard_strided.argtypes = [P, P, P, i64, P]
         L.adamw_fp8_step.argtypes = [P, P, P, P, P, P, i64, C.POINTER(AdamW), P]
         L.fold_adamw_fp8_step.argtypes = [P, P, P, P, P, P, P, C.POINTER(AdamW), P]
         L.fold_adamw_fp8_step_unpack.argtypes = [P, P, P, P, P, P, P, P, P, C.POINTER(AdamW), P]
@@ -88,6 +91,47 @@ def _dev(t, dtype, name, numel=None):
     if numel is not None and t.numel() < numel:
         raise ValueError(f"{name}: needs at least {numel} elements, has {t.numel()}")
     return C.c_void_p(t.data_ptr())
+
+
+def _tile_array(t, q, name):
+    """(pointer, tile stride in floats or None) of a shard array of q FP32
+    tiles: a contiguous tensor of at least q * 16384 elements (stride
+    16384), or a 2-D view (>= q, 16384) whose rows are the tiles, strides
+    (S, 1) -- e.g. state[:, 0] of a (q, 3, 16384) tensor, the interleaved
+    layout.  A single-row view has no stride of its own (None)."""
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float32:
+        raise TypeError(f"{name}: need a float32 CUDA tensor")
+    if t.dim() == 2 and t.shape[1] == TILE_ELEMS and t.stride(1) == 1:
+        if t.shape[0] < q:
+            raise ValueError(f"{name}: needs at least {q} tiles, has {t.shape[0]}")
+        return C.c_void_p(t.data_ptr()), (t.stride(0) if t.shape[0] > 1 else None)
+    if t.is_contiguous():
+        if t.numel() < q * TILE_ELEMS:
+            raise ValueError(f"{name}: needs at least {q * TILE_ELEMS} elements, has {t.numel()}")
+        return C.c_void_p(t.data_ptr()), TILE_ELEMS
+    raise TypeError(f"{name}: need a contiguous tensor or a (tiles, 16384) view of unit inner stride")
+
+
+def _state(master, m, v, q, hp):
+    """Pointers of master, m, v and a copy of hp whose state_stride is their
+    common tile stride (they must agree; irrelevant when q <= 1)."""
+    if isinstance(hp, dict):
+        hp = AdamW(**hp)
+    arrs = [_tile_array(t, q, n) for t, n in ((master, "master"), (m, "m"), (v, "v"))]
+    strides = {st for _, st in arrs if st is not None}
+    if q <= 1 or not strides:
+        stride = TILE_ELEMS
+    elif len(strides) == 1:
+        stride = strides.pop()
+    else:
+        raise ValueError(f"master, m and v have different tile strides {sorted(strides)}")
+    if hp.state_stride not in (0, stride):
+        raise ValueError(f"hp.state_stride {hp.state_stride} disagrees with the tensors' tile "
+                         f"stride {stride}")
+    hp = AdamW.from_buffer_copy(hp)
+    hp.state_stride = 0 if stride == TILE_ELEMS else stride
+    return [a for a, _ in arrs], hp
 
 
 class Plan:
@@ -174,26 +218,37 @@ def _ptr_array(tensors, dtype, name, n):
 
 def pack_shard(plan: Plan, srcs, dst, stream=None):
     """Fold the weights' row-major FP32 tensors (srcs[p], or None for weights
-    the rank does not touch) into the tile-major shard dst (q * 16384 floats)."""
+    the rank does not touch) into the tile-major shard dst: q * 16384
+    contiguous floats (pack_shard), or a (>= q, 16384) view whose tiles sit
+    S floats apart, e.g. master = state[:, 0] of the interleaved layout
+    (pack_shard_strided)."""
     import torch
     arr = _ptr_array(srcs, torch.float32, "srcs", len(plan.dims))
-    d = _dev(dst, torch.float32, "dst", plan.shard_tiles * TILE_ELEMS)
-    _check(lib().pack_shard(plan.handle, C.cast(arr, C.c_void_p), d, _stream(stream)))
+    d, stride = _tile_array(dst, plan.shard_tiles, "dst")
+    if stride in (None, TILE_ELEMS):
+        _check(lib().pack_shard(plan.handle, C.cast(arr, C.c_void_p), d, _stream(stream)))
+    else:
+        _check(lib().pack_shard_strided(plan.handle, C.cast(arr, C.c_void_p), d, stride,
+                                        _stream(stream)))
 
 
 def adamw_fp8_step(master, grad, m, v, codes, scale_inv, hp, n_tiles=None, stream=None):
     """Fused AdamW + per-tile E4M3 requant over n_tiles whole tiles (default:
-    all of master).  hp: AdamW, or a dict of its fields."""
+    all of master).  hp: AdamW, or a dict of its fields.  master / m / v:
+    contiguous, or (tiles, 16384) views with a common tile stride (the
+    interleaved layout: state[:, 0], state[:, 1], state[:, 2] of a
+    (q, 3, 16384) tensor)."""
     import torch
-    if isinstance(hp, dict):
-        hp = AdamW(**hp)
     if n_tiles is None:
-        if master.numel() % TILE_ELEMS:
+        if master.dim() == 2 and master.shape[1] == TILE_ELEMS:
+            n_tiles = master.shape[0]
+        elif master.numel() % TILE_ELEMS:
             raise ValueError("master is not a whole number of tiles")
-        n_tiles = master.numel() // TILE_ELEMS
+        else:
+            n_tiles = master.numel() // TILE_ELEMS
     n = n_tiles * TILE_ELEMS
-    args = [_dev(master, torch.float32, "master", n), _dev(grad, torch.float32, "grad", n),
-            _dev(m, torch.float32, "m", n), _dev(v, torch.float32, "v", n),
+    (p, mm, vv), hp = _state(master, m, v, n_tiles, hp)
+    args = [p, _dev(grad, torch.float32, "grad", n), mm, vv,
             _dev(codes, torch.uint8, "codes", n), _dev(scale_inv, torch.float32, "scale_inv", n_tiles)]
     _check(lib().adamw_fp8_step(*args, n_tiles, C.byref(hp), _stream(stream)))
 
@@ -202,13 +257,11 @@ def fold_adamw_fp8_step(plan: Plan, grads, master, m, v, codes, scale_inv, hp, s
     """pack_shard of the row-major gradients grads[p] and adamw_fp8_step over
     the whole shard in one pass (the folded gradient is never stored)."""
     import torch
-    if isinstance(hp, dict):
-        hp = AdamW(**hp)
     arr = _ptr_array(grads, torch.float32, "grads", len(plan.dims))
     q = plan.shard_tiles
     n = q * TILE_ELEMS
-    args = [_dev(master, torch.float32, "master", n), _dev(m, torch.float32, "m", n),
-            _dev(v, torch.float32, "v", n), _dev(codes, torch.uint8, "codes", n),
+    (p, mm, vv), hp = _state(master, m, v, q, hp)
+    args = [p, mm, vv, _dev(codes, torch.uint8, "codes", n),
             _dev(scale_inv, torch.float32, "scale_inv", q)]
     _check(lib().fold_adamw_fp8_step(plan.handle, C.cast(arr, C.c_void_p), *args, C.byref(hp),
                                      _stream(stream)))
@@ -219,8 +272,6 @@ def fold_adamw_fp8_step_unpack(plan: Plan, grads, master, m, v, codes, scale_inv
     """fold_adamw_fp8_step and unpack_fp8 in one pass.  codes / scale_inv may
     both be None (no tile-major copy of the codes)."""
     import torch
-    if isinstance(hp, dict):
-        hp = AdamW(**hp)
     if (codes is None) != (scale_inv is None):
         raise ValueError("codes and scale_inv: give both or neither")
     n = len(plan.dims)
@@ -230,9 +281,9 @@ def fold_adamw_fp8_step_unpack(plan: Plan, grads, master, m, v, codes, scale_inv
     asc = _ptr_array(dst_scale, torch.float32, "dst_scale", n)
     c = None if codes is None else _dev(codes, torch.uint8, "codes", q * TILE_ELEMS)
     sc = None if scale_inv is None else _dev(scale_inv, torch.float32, "scale_inv", q)
+    (p, mm, vv), hp = _state(master, m, v, q, hp)
     _check(lib().fold_adamw_fp8_step_unpack(
-        plan.handle, C.cast(g, C.c_void_p), _dev(master, torch.float32, "master", q * TILE_ELEMS),
-        _dev(m, torch.float32, "m", q * TILE_ELEMS), _dev(v, torch.float32, "v", q * TILE_ELEMS),
+        plan.handle, C.cast(g, C.c_void_p), p, mm, vv,
         c, sc, C.cast(a8, C.c_void_p), C.cast(asc, C.c_void_p), C.byref(hp), _stream(stream)))
 
 
@@ -242,8 +293,6 @@ def fold_adamw_fp8_step_unpack_t(plan: Plan, grads, master, m, v, codes, scale_i
     copy (dst_t[p] uint8 (E, W, H), dst_t_scale[p] float32 (E, W, ceil(H/128)))
     in one pass.  hp must have scale_pow2 set; codes / scale_inv may both be None."""
     import torch
-    if isinstance(hp, dict):
-        hp = AdamW(**hp)
     if (codes is None) != (scale_inv is None):
         raise ValueError("codes and scale_inv: give both or neither")
     n = len(plan.dims)
@@ -255,9 +304,9 @@ def fold_adamw_fp8_step_unpack_t(plan: Plan, grads, master, m, v, codes, scale_i
     tsc = _ptr_array(dst_t_scale, torch.float32, "dst_t_scale", n)
     c = None if codes is None else _dev(codes, torch.uint8, "codes", q * TILE_ELEMS)
     sc = None if scale_inv is None else _dev(scale_inv, torch.float32, "scale_inv", q)
+    (p, mm, vv), hp = _state(master, m, v, q, hp)
     _check(lib().fold_adamw_fp8_step_unpack_t(
-        plan.handle, C.cast(g, C.c_void_p), _dev(master, torch.float32, "master", q * TILE_ELEMS),
-        _dev(m, torch.float32, "m", q * TILE_ELEMS), _dev(v, torch.float32, "v", q * TILE_ELEMS),
+        plan.handle, C.cast(g, C.c_void_p), p, mm, vv,
         c, sc, C.cast(a8, C.c_void_p), C.cast(asc, C.c_void_p), C.cast(t8, C.c_void_p),
         C.cast(tsc, C.c_void_p), C.byref(hp), _stream(stream)))
 

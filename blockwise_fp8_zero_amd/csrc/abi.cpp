@@ -66,24 +66,50 @@ using namespace bfz;
 
 extern "C" const char* bfz_last_error(void) { return g_last_error; }
 
-extern "C" int pack_shard(const bfz_plan* plan, const float* const* src, float* dst, void* stream) {
-    if (!plan || !src || !dst) return fail(BFZ_EINVAL, "pack_shard: null pointer");
-    int rc = check_plan(plan, "pack_shard");
+namespace {
+
+// Tiles of a strided shard array (master, m, v) sit `stride` floats apart:
+// at least a tile, whole float4 (16-byte aligned tiles), and at most 2^26
+// so that slot * stride stays far inside 64 bits.
+constexpr int64_t kMaxStateStride = int64_t(1) << 26;
+
+bool valid_stride(int64_t stride) {
+    return stride >= kTileElems && stride <= kMaxStateStride && stride % 4 == 0;
+}
+
+int fold(const bfz_plan* plan, const float* const* src, float* dst, int64_t dst_stride,
+         void* stream, const char* where) {
+    if (!plan || !src || !dst) return fail(BFZ_EINVAL, "%s: null pointer", where);
+    if (!valid_stride(dst_stride))
+        return fail(BFZ_EINVAL, "%s: dst_stride %lld is not a multiple of 4 in [16384, 2^26]", where,
+                    (long long)dst_stride);
+    int rc = check_plan(plan, where);
     if (rc) return rc;
-    if (!aligned(dst, 16)) return fail(BFZ_EALIGN, "pack_shard: dst must be 16-byte aligned");
-    rc = check_weights(plan, reinterpret_cast<const void* const*>(src), "pack_shard");
+    if (!aligned(dst, 16)) return fail(BFZ_EALIGN, "%s: dst must be 16-byte aligned", where);
+    rc = check_weights(plan, reinterpret_cast<const void* const*>(src), where);
     if (rc) return rc;
     for (int32_t w = 0; w < plan->n_weights; ++w)
         if (src[w] && !aligned(src[w], 4))
-            return fail(BFZ_EALIGN, "pack_shard: weight %d must be 4-byte aligned", w);
+            return fail(BFZ_EALIGN, "%s: weight %d must be 4-byte aligned", where, w);
     for (const Segment& seg : plan->segments) {
         PackArgs args{};
         for (int32_t k = 0; k < seg.n_weights; ++k) args.src[k] = src[seg.weight0 + k];
-        int err = launch_pack(plan->d_entries + seg.slot0, seg.n_slots,
-                              dst + seg.slot0 * kTileElems, args, stream);
-        if (err != hipSuccess) return hip_fail("pack_shard", err);
+        int err = launch_pack(plan->d_entries + seg.slot0, seg.n_slots, dst + seg.slot0 * dst_stride,
+                              dst_stride, args, stream);
+        if (err != hipSuccess) return hip_fail(where, err);
     }
     return BFZ_OK;
+}
+
+}  // namespace
+
+extern "C" int pack_shard(const bfz_plan* plan, const float* const* src, float* dst, void* stream) {
+    return fold(plan, src, dst, kTileElems, stream, "pack_shard");
+}
+
+extern "C" int pack_shard_strided(const bfz_plan* plan, const float* const* src, float* dst,
+                                  int64_t dst_stride, void* stream) {
+    return fold(plan, src, dst, dst_stride, stream, "pack_shard_strided");
 }
 
 extern "C" int unpack_fp8(const bfz_plan* plan, const uint8_t* codes, const float* scale_inv,
@@ -121,6 +147,10 @@ namespace {
 // the bias corrections 1 - beta^t enter as lr / (1 - beta1^t) and
 // sqrt(1 - beta2^t), as in the Int8AdamW step (lpnh.cn essay, section 4.3).
 int make_scalars(const bfz_adamw* hp, StepScalars* s, const char* where) {
+    s->state_stride = hp->state_stride == 0 ? kTileElems : hp->state_stride;
+    if (!valid_stride(s->state_stride))
+        return fail(BFZ_EINVAL, "%s: state_stride %lld is not 0 or a multiple of 4 in [16384, 2^26]",
+                    where, (long long)hp->state_stride);
     const double lr = hp->lr, b1 = hp->beta1, b2 = hp->beta2, eps = hp->eps, wd = hp->weight_decay;
     if (!std::isfinite(lr) || !std::isfinite(eps) || !std::isfinite(wd) || !(eps >= 0.0) ||
         !(b1 >= 0.0 && b1 < 1.0) || !(b2 >= 0.0 && b2 < 1.0) || hp->step < 1)
@@ -190,9 +220,9 @@ extern "C" int fold_adamw_fp8_step(const bfz_plan* plan, const float* const* gra
     for (const Segment& seg : plan->segments) {
         PackArgs args{};
         for (int32_t k = 0; k < seg.n_weights; ++k) args.src[k] = grad[seg.weight0 + k];
-        const int64_t off = seg.slot0 * kTileElems;
-        int err = launch_fold_step(plan->d_entries + seg.slot0, seg.n_slots, args, master + off,
-                                   m + off, v + off, codes + off, scale_inv + seg.slot0, s, stream);
+        const int64_t off = seg.slot0 * kTileElems, soff = seg.slot0 * s.state_stride;
+        int err = launch_fold_step(plan->d_entries + seg.slot0, seg.n_slots, args, master + soff,
+                                   m + soff, v + soff, codes + off, scale_inv + seg.slot0, s, stream);
         if (err != hipSuccess) return hip_fail("fold_adamw_fp8_step", err);
     }
     return BFZ_OK;
@@ -235,9 +265,9 @@ extern "C" int fold_adamw_fp8_step_unpack(const bfz_plan* plan, const float* con
             out.codes[k] = dst_fp8[seg.weight0 + k];
             out.scale[k] = dst_scale[seg.weight0 + k];
         }
-        const int64_t off = seg.slot0 * kTileElems;
+        const int64_t off = seg.slot0 * kTileElems, soff = seg.slot0 * s.state_stride;
         int err = launch_fold_step_unfold(plan->d_entries + seg.slot0, seg.n_slots, in, out,
-                                          master + off, m + off, v + off,
+                                          master + soff, m + soff, v + soff,
                                           codes ? codes + off : nullptr,
                                           scale_inv ? scale_inv + seg.slot0 : nullptr, s, stream);
         if (err != hipSuccess) return hip_fail(where, err);
@@ -295,9 +325,9 @@ extern "C" int fold_adamw_fp8_step_unpack_t(const bfz_plan* plan, const float* c
             tout.scale[k] = dst_t_scale[seg.weight0 + k];
             tout.rows[k] = int32_t(plan->dims[3 * (seg.weight0 + k) + 1]);
         }
-        const int64_t off = seg.slot0 * kTileElems;
+        const int64_t off = seg.slot0 * kTileElems, soff = seg.slot0 * s.state_stride;
         int err = launch_fold_step_unfold_t(plan->d_entries + seg.slot0, seg.n_slots, in, out, tout,
-                                            master + off, m + off, v + off,
+                                            master + soff, m + soff, v + soff,
                                             codes ? codes + off : nullptr,
                                             scale_inv ? scale_inv + seg.slot0 : nullptr, s, stream);
         if (err != hipSuccess) return hip_fail(where, err);

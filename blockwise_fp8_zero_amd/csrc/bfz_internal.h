@@ -49,16 +49,18 @@ struct TransposeArgs {
     int32_t rows[kSegWeights];    // H of each weight
 };
 
-// FP32 scalars of one AdamW step, rounded once from double.
+// What the step kernels need of one step: the FP32 scalars, rounded once
+// from double, the options, and the state layout.
 struct StepScalars {
     float b1, c1, b2, c2, step_size, sbc2, eps, decay;
     int32_t has_decay;
-    int32_t pow2;  // power-of-two tile scales
+    int32_t pow2;          // power-of-two tile scales
+    int64_t state_stride;  // floats from one tile of master / m / v to the next
 };
 
 // Kernel launchers (kernels.hip).  They return a hipError_t value as int.
-int launch_pack(const TileEntry* d_entries, int64_t n_slots, float* dst, const PackArgs& args,
-                void* stream);
+int launch_pack(const TileEntry* d_entries, int64_t n_slots, float* dst, int64_t dst_stride,
+                const PackArgs& args, void* stream);
 int launch_unpack(const TileEntry* d_entries, int64_t n_slots, const uint8_t* codes,
                   const float* scale_inv, const UnpackArgs& args, void* stream);
 int launch_step(float* master, const float* grad, float* m, float* v, uint8_t* codes,

@@ -218,10 +218,13 @@ __device__ __forceinline__ float step_tile(int64_t tile, float* __restrict__ mas
                                            float* __restrict__ scale_inv, const StepScalars& s,
                                            const GradFn& grad_at, float* wave_amax,
                                            const Out& out = Out{}) {
+    // master / m / v tiles sit state_stride floats apart (16384: separate
+    // arrays; 49152: one [master | m | v] block per tile); codes are tile-major
     const int64_t base = tile * (kTileElems / 4);
-    f32x4* P = reinterpret_cast<f32x4*>(master) + base;
-    f32x4* M = reinterpret_cast<f32x4*>(mom1) + base;
-    f32x4* V = reinterpret_cast<f32x4*>(mom2) + base;
+    const int64_t sbase = tile * (s.state_stride / 4);
+    f32x4* P = reinterpret_cast<f32x4*>(master) + sbase;
+    f32x4* M = reinterpret_cast<f32x4*>(mom1) + sbase;
+    f32x4* V = reinterpret_cast<f32x4*>(mom2) + sbase;
 
     f32x4 p[kStepVec], g[kStepVec], m[kStepVec], v[kStepVec];
 #pragma unroll
@@ -336,12 +339,14 @@ __global__ __launch_bounds__(kStepThreads) void fold_step_unfold_kernel(
 // layout: thread t moves float4 column t % 32 of rows t / 32 + 32 k, k < 4,
 // so a wave covers two 512-byte tile rows per instruction on both sides.
 // All four loads are issued before the stores; streaming accesses.  Outside
-// the weight's edge, and in padding slots, the tile gets +0.0.
+// the weight's edge, and in padding slots, the tile gets +0.0.  Slot s is
+// written at dst + s * dst_stride.
 __global__ __launch_bounds__(kStepThreads) void pack_kernel(const TileEntry* __restrict__ entries,
-                                                            float* __restrict__ dst, PackArgs args) {
+                                                            float* __restrict__ dst, int64_t dst_stride,
+                                                            PackArgs args) {
     const int64_t slot = xcd_tile(blockIdx.x, gridDim.x);
     const TileEntry t = entries[slot];
-    f32x4* out = reinterpret_cast<f32x4*>(dst + slot * kTileElems);
+    f32x4* out = reinterpret_cast<f32x4*>(dst + slot * dst_stride);
     RowMajorGrad src{nullptr, t.ld, t.valid_rows, t.valid_cols, false};
     if (t.local >= 0) {
         const float* w = args.src[t.local];
@@ -805,11 +810,11 @@ int launch_fold_step_unfold(const TileEntry* d_entries, int64_t n_slots, const P
     return hipGetLastError();
 }
 
-int launch_pack(const TileEntry* d_entries, int64_t n_slots, float* dst, const PackArgs& args,
-                void* stream) {
+int launch_pack(const TileEntry* d_entries, int64_t n_slots, float* dst, int64_t dst_stride,
+                const PackArgs& args, void* stream) {
     if (n_slots == 0) return hipSuccess;
     hipLaunchKernelGGL(pack_kernel, dim3((uint32_t)n_slots), dim3(kStepThreads), 0,
-                       (hipStream_t)stream, d_entries, dst, args);
+                       (hipStream_t)stream, d_entries, dst, dst_stride, args);
     return hipGetLastError();
 }
 

@@ -23,15 +23,24 @@ class GpuWorkload:
 
     MODES = ("unfused", "fused", "fused_unpack")
 
-    def __init__(self, w: WL.Workload, device="cuda", mode="unfused", pow2=False, transposed=False):
+    LAYOUTS = ("separate", "interleaved")
+
+    def __init__(self, w: WL.Workload, device="cuda", mode="unfused", pow2=False, transposed=False,
+                 layout="separate"):
         """mode: how a step is taken --
         "unfused": pack_shard + adamw_fp8_step (then unpack_fp8 on demand);
         "fused": fold_adamw_fp8_step (gradients read row-major);
         "fused_unpack": fold_adamw_fp8_step_unpack, which also writes the
         row-major FP8 weights and scale grids (self.out_fp8 / self.out_scale).
         transposed (fused_unpack with pow2 only): fold_adamw_fp8_step_unpack_t,
-        which also writes W^T and its group scales (self.out_t / self.out_t_scale)."""
+        which also writes W^T and its group scales (self.out_t / self.out_t_scale).
+        layout: the FP32 state -- "separate": master, m, v are three
+        tile-major arrays; "interleaved": one (q, 3, 16384) tensor, each
+        tile's [master | m | v] contiguous, passed as its three (q, 16384)
+        views (state_stride 49152)."""
         assert mode in self.MODES, mode
+        assert layout in self.LAYOUTS, layout
+        self.layout = layout
         assert not transposed or (mode == "fused_unpack" and pow2), "transposed: fused_unpack + pow2"
         self.transposed = transposed
         self.w = w
@@ -48,10 +57,14 @@ class GpuWorkload:
         self.ranges = {p: WL.rows_touched(owned_rows, p, w.dims) for p in self.touched}
         n = self.q * TILE_ELEMS
         kw = dict(device=self.device)
-        self.master = torch.empty(n, dtype=torch.float32, **kw)
+        if layout == "interleaved":
+            self.state = torch.empty((self.q, 3, TILE_ELEMS), dtype=torch.float32, **kw)
+            self.master, self.m, self.v = self.state[:, 0], self.state[:, 1], self.state[:, 2]
+        else:
+            self.master = torch.empty(n, dtype=torch.float32, **kw)
+            self.m = torch.empty(n, dtype=torch.float32, **kw)
+            self.v = torch.empty(n, dtype=torch.float32, **kw)
         self.grad = torch.empty(n, dtype=torch.float32, **kw)
-        self.m = torch.empty(n, dtype=torch.float32, **kw)
-        self.v = torch.empty(n, dtype=torch.float32, **kw)
         self.codes = torch.empty(n, dtype=torch.uint8, **kw)
         self.scale_inv = torch.empty(self.q, dtype=torch.float32, **kw)
         self.grad_rm = None

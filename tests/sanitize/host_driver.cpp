@@ -85,11 +85,12 @@ int record(const bfz::TileEntry* e, int64_t n) {
 
 namespace bfz {
 
-int launch_pack(const TileEntry* e, int64_t n, float* dst, const PackArgs& args, void*) {
+int launch_pack(const TileEntry* e, int64_t n, float* dst, int64_t dst_stride, const PackArgs& args,
+                void*) {
     if (int err = record(e, n)) return err;
     for (int64_t s = 0; s < n; ++s) {
         const TileEntry& t = e[s];
-        float* tile = dst + s * kTileElems;
+        float* tile = dst + s * dst_stride;
         for (int a = 0; a < kTileDim; ++a)
             for (int b = 0; b < kTileDim; ++b)
                 tile[a * kTileDim + b] = (t.local >= 0 && a < t.valid_rows && b < t.valid_cols)
@@ -114,28 +115,32 @@ int launch_unpack(const TileEntry* e, int64_t n, const uint8_t* codes, const flo
 }
 
 // The step's arithmetic is not what is checked here: each element of every
-// array is read and written once (p += g, m and v touched, code = low byte
-// of p's bits, scale_inv = 1), so the sanitizer sees the kernel's extents.
+// array is read and written once (p += g, m += p, v = m - g, code = low byte
+// of p's bits, scale_inv = 1), so the sanitizer sees the kernel's extents
+// and a result that depends on every array's placement.  master / m / v
+// tiles sit `stride` floats apart, gradient and code tiles 16384.
 static void touch_tile(float* p, const float* g, float* m, float* v, uint8_t* codes, float* sc,
-                       int64_t s) {
+                       int64_t s, int64_t stride) {
     for (int k = 0; k < kTileElems; ++k) {
-        const int64_t i = s * kTileElems + k;
-        p[i] += g ? g[i] : 0.0f;
-        m[i] = m[i];
-        v[i] = v[i];
+        const int64_t i = s * stride + k, j = s * kTileElems + k;
+        const float gi = g ? g[j] : 0.0f;
+        p[i] += gi;
+        m[i] += p[i];
+        v[i] = m[i] - gi;
         if (codes) {
             uint32_t bits;
             std::memcpy(&bits, &p[i], 4);
-            codes[i] = uint8_t(bits);
+            codes[j] = uint8_t(bits);
         }
     }
     if (sc) sc[s] = 1.0f;
 }
 
 int launch_step(float* master, const float* grad, float* m, float* v, uint8_t* codes,
-                float* scale_inv, int64_t n_tiles, const StepScalars&, void*) {
+                float* scale_inv, int64_t n_tiles, const StepScalars& st, void*) {
     g_calls.push_back({nullptr, n_tiles});
-    for (int64_t s = 0; s < n_tiles; ++s) touch_tile(master, grad, m, v, codes, scale_inv, s);
+    for (int64_t s = 0; s < n_tiles; ++s)
+        touch_tile(master, grad, m, v, codes, scale_inv, s, st.state_stride);
     return 0;
 }
 
@@ -147,32 +152,32 @@ static void fold_grad(const TileEntry& t, const float* src, std::vector<float>& 
 }
 
 int launch_fold_step(const TileEntry* e, int64_t n, const PackArgs& grads, float* master, float* m,
-                     float* v, uint8_t* codes, float* scale_inv, const StepScalars&, void*) {
+                     float* v, uint8_t* codes, float* scale_inv, const StepScalars& st, void*) {
     if (int err = record(e, n)) return err;
     std::vector<float> g;
     for (int64_t s = 0; s < n; ++s) {
         fold_grad(e[s], e[s].local >= 0 ? grads.src[e[s].local] : nullptr, g);
-        for (int k = 0; k < kTileElems; ++k) master[s * kTileElems + k] += g[k];
-        touch_tile(master, nullptr, m, v, codes, scale_inv, s);
+        for (int k = 0; k < kTileElems; ++k) master[s * st.state_stride + k] += g[k];
+        touch_tile(master, nullptr, m, v, codes, scale_inv, s, st.state_stride);
     }
     return 0;
 }
 
 int launch_fold_step_unfold(const TileEntry* e, int64_t n, const PackArgs& grads,
                             const UnpackArgs& outs, float* master, float* m, float* v,
-                            uint8_t* codes, float* scale_inv, const StepScalars&, void*) {
+                            uint8_t* codes, float* scale_inv, const StepScalars& st, void*) {
     if (int err = record(e, n)) return err;
     std::vector<float> g;
     for (int64_t s = 0; s < n; ++s) {
         const TileEntry& t = e[s];
         fold_grad(t, t.local >= 0 ? grads.src[t.local] : nullptr, g);
-        for (int k = 0; k < kTileElems; ++k) master[s * kTileElems + k] += g[k];
-        touch_tile(master, nullptr, m, v, codes, scale_inv, s);
+        for (int k = 0; k < kTileElems; ++k) master[s * st.state_stride + k] += g[k];
+        touch_tile(master, nullptr, m, v, codes, scale_inv, s, st.state_stride);
         if (t.local < 0) continue;
         for (int a = 0; a < t.valid_rows; ++a)
             for (int b = 0; b < t.valid_cols; ++b) {
                 uint32_t bits;
-                std::memcpy(&bits, &master[s * kTileElems + a * kTileDim + b], 4);
+                std::memcpy(&bits, &master[s * st.state_stride + a * kTileDim + b], 4);
                 outs.codes[t.local][t.base + (int64_t)a * t.ld + b] = uint8_t(bits);
             }
         outs.scale[t.local][t.scale_index] = 1.0f;
@@ -199,7 +204,7 @@ int launch_fold_step_unfold_t(const TileEntry* e, int64_t n, const PackArgs& gra
             const int64_t out_row = ex * W + kTileDim * j + c;
             for (int r = 0; r < t.valid_rows; ++r) {
                 uint32_t bits;
-                std::memcpy(&bits, &master[sl * kTileElems + r * kTileDim + c], 4);
+                std::memcpy(&bits, &master[sl * s.state_stride + r * kTileDim + c], 4);
                 touts.codes[t.local][out_row * H + kTileDim * i + r] = uint8_t(bits);
             }
             touts.scale[t.local][out_row * hb + i] = 1.0f;
@@ -412,7 +417,7 @@ void run_plan_case(const std::vector<int64_t>& dims, int32_t D) {
                           "transposed element");
         }
         // the step entry points reach every slot of the shard
-        bfz_adamw hp{1e-4, 0.9, 0.95, 1e-8, 0.1, 1, 0};
+        bfz_adamw hp{1e-4, 0.9, 0.95, 1e-8, 0.1, 1, 0, 0};
         g_calls.clear();
         CHECK(adamw_fp8_step(shard, shard, m, v, codes, sc, q, &hp, nullptr) == BFZ_OK, "step: %s", bfz_last_error());
         g_calls.clear();
@@ -468,6 +473,114 @@ void run_plan_case(const std::vector<int64_t>& dims, int32_t D) {
     CHECK(seen == T, "ranks own %lld of %lld tiles", (long long)seen, (long long)T);
 }
 
+// The interleaved state layout (state_stride 49152: one [master | m | v]
+// block per tile, allocated at its exact size) against three separate
+// arrays: the same folds and steps must leave bit-identical state, codes,
+// scales and row-major outputs in every route, so a launch segment given
+// the wrong state offset shows up -- and any access past the block buffer
+// is a sanitizer report.
+void run_layout_case(const std::vector<int64_t>& dims, int32_t D) {
+    const int32_t n = int32_t(dims.size() / 3);
+    constexpr int64_t S = 3 * kTileElems;
+    for (int32_t rank = 0; rank < D; ++rank) {
+        bfz_plan* plan = nullptr;
+        CHECK(bfz_plan_create(dims.data(), n, D, rank, &plan) == BFZ_OK, "plan_create: %s", bfz_last_error());
+        if (!plan) return;
+        CHECK(bfz_plan_upload(plan) == BFZ_OK, "upload");
+        const int64_t q = bfz_plan_shard_tiles(plan), ne = q * kTileElems;
+        const size_t nw = size_t(n);
+        std::vector<float*> w(nw), gr(nw);
+        std::vector<uint8_t*> w8a(nw), w8b(nw), wta(nw), wtb(nw);
+        std::vector<float*> ga(nw), gb(nw), tga(nw), tgb(nw);
+        for (int32_t p = 0; p < n; ++p) {
+            const int64_t E = dims[3 * p], H = dims[3 * p + 1], W = dims[3 * p + 2];
+            const int64_t cells = E * ((H + 127) / 128) * ((W + 127) / 128), tcells = E * W * ((H + 127) / 128);
+            w[size_t(p)] = exact<float>(E * H * W);
+            gr[size_t(p)] = exact<float>(E * H * W);
+            for (int64_t k = 0; k < E * H * W; ++k) {
+                w[size_t(p)][k] = float(p + 1) + float(k % 1021) * 0.25f;
+                gr[size_t(p)][k] = float(k % 7) - 3.0f;
+            }
+            for (auto* v8 : {&w8a, &w8b, &wta, &wtb}) {
+                (*v8)[size_t(p)] = exact<uint8_t>(E * H * W);
+                std::memset((*v8)[size_t(p)], 0, size_t(E * H * W));
+            }
+            for (auto* vg : {&ga, &gb}) {
+                (*vg)[size_t(p)] = exact<float>(cells);
+                std::memset((*vg)[size_t(p)], 0, size_t(cells) * 4);
+            }
+            for (auto* vg : {&tga, &tgb}) {
+                (*vg)[size_t(p)] = exact<float>(tcells);
+                std::memset((*vg)[size_t(p)], 0, size_t(tcells) * 4);
+            }
+        }
+        const float* const* wc = const_cast<const float* const*>(w.data());
+        const float* const* gc = const_cast<const float* const*>(gr.data());
+        float* P = exact<float>(ne);
+        float* M = exact<float>(ne);
+        float* V = exact<float>(ne);
+        float* state = exact<float>(q * S);
+        float* grad = exact<float>(ne);
+        uint8_t* ca = exact<uint8_t>(ne);
+        uint8_t* cb = exact<uint8_t>(ne);
+        float* sa = exact<float>(q);
+        float* sb = exact<float>(q);
+        // fold master, m and v (the same weights, so m = v = master to start)
+        for (float* x : {P, M, V}) CHECK(pack_shard(plan, wc, x, nullptr) == BFZ_OK, "pack: %s", bfz_last_error());
+        for (int64_t off : {int64_t(0), int64_t(kTileElems), int64_t(2 * kTileElems)})
+            CHECK(pack_shard_strided(plan, wc, state + off, S, nullptr) == BFZ_OK, "pack strided: %s",
+                  bfz_last_error());
+        CHECK(pack_shard(plan, gc, grad, nullptr) == BFZ_OK, "pack grad");
+        g_calls.clear();
+        bfz_adamw hs{1e-4, 0.9, 0.95, 1e-8, 0.1, 1, 0, 0};
+        bfz_adamw hi = hs;
+        hi.state_stride = S;
+        float *Pi = state, *Mi = state + kTileElems, *Vi = state + 2 * kTileElems;
+        CHECK(adamw_fp8_step(P, grad, M, V, ca, sa, q, &hs, nullptr) == BFZ_OK, "step");
+        CHECK(adamw_fp8_step(Pi, grad, Mi, Vi, cb, sb, q, &hi, nullptr) == BFZ_OK, "step interleaved: %s",
+              bfz_last_error());
+        CHECK(fold_adamw_fp8_step(plan, gc, P, M, V, ca, sa, &hs, nullptr) == BFZ_OK, "fold step");
+        CHECK(fold_adamw_fp8_step(plan, gc, Pi, Mi, Vi, cb, sb, &hi, nullptr) == BFZ_OK, "fold step interleaved");
+        CHECK(fold_adamw_fp8_step_unpack(plan, gc, P, M, V, ca, sa, w8a.data(), ga.data(), &hs, nullptr) == BFZ_OK,
+              "one-kernel step");
+        CHECK(fold_adamw_fp8_step_unpack(plan, gc, Pi, Mi, Vi, cb, sb, w8b.data(), gb.data(), &hi, nullptr) ==
+                  BFZ_OK,
+              "one-kernel step interleaved");
+        hs.scale_pow2 = hi.scale_pow2 = 1;
+        CHECK(fold_adamw_fp8_step_unpack_t(plan, gc, P, M, V, ca, sa, w8a.data(), ga.data(), wta.data(),
+                                           tga.data(), &hs, nullptr) == BFZ_OK,
+              "transposed-copy step");
+        CHECK(fold_adamw_fp8_step_unpack_t(plan, gc, Pi, Mi, Vi, cb, sb, w8b.data(), gb.data(), wtb.data(),
+                                           tgb.data(), &hi, nullptr) == BFZ_OK,
+              "transposed-copy step interleaved");
+        g_calls.clear();
+        for (int64_t sl = 0; sl < q; ++sl) {
+            CHECK(std::memcmp(P + sl * kTileElems, Pi + sl * S, kTileElems * 4) == 0 &&
+                      std::memcmp(M + sl * kTileElems, Mi + sl * S, kTileElems * 4) == 0 &&
+                      std::memcmp(V + sl * kTileElems, Vi + sl * S, kTileElems * 4) == 0,
+                  "rank %d slot %lld: interleaved state differs from separate arrays", rank, (long long)sl);
+        }
+        CHECK(std::memcmp(ca, cb, size_t(ne)) == 0 && std::memcmp(sa, sb, size_t(q) * 4) == 0, "codes / scales");
+        for (int32_t p = 0; p < n; ++p) {
+            const int64_t E = dims[3 * p], H = dims[3 * p + 1], W = dims[3 * p + 2];
+            const int64_t cells = E * ((H + 127) / 128) * ((W + 127) / 128), tcells = E * W * ((H + 127) / 128);
+            CHECK(std::memcmp(w8a[size_t(p)], w8b[size_t(p)], size_t(E * H * W)) == 0 &&
+                      std::memcmp(wta[size_t(p)], wtb[size_t(p)], size_t(E * H * W)) == 0 &&
+                      std::memcmp(ga[size_t(p)], gb[size_t(p)], size_t(cells) * 4) == 0 &&
+                      std::memcmp(tga[size_t(p)], tgb[size_t(p)], size_t(tcells) * 4) == 0,
+                  "row-major outputs of weight %d", p);
+            for (auto* v : {&w8a, &w8b, &wta, &wtb}) std::free((*v)[size_t(p)]);
+            for (auto* v : {&ga, &gb, &tga, &tgb}) std::free((*v)[size_t(p)]);
+            std::free(w[size_t(p)]);
+            std::free(gr[size_t(p)]);
+        }
+        for (void* x : {(void*)P, (void*)M, (void*)V, (void*)state, (void*)grad, (void*)ca, (void*)cb, (void*)sa,
+                        (void*)sb})
+            std::free(x);
+        bfz_plan_destroy(plan);
+    }
+}
+
 void run_error_paths() {
     const int64_t dims[] = {1, 200, 130};
     bfz_plan* plan = nullptr;
@@ -509,7 +622,7 @@ void run_error_paths() {
     float* w = exact<float>(200 * 130 + 1);
     uint8_t* w8 = exact<uint8_t>(200 * 130 + 1);
     float* g = exact<float>(2 * 2 + 1);
-    bfz_adamw hp{1e-4, 0.9, 0.95, 1e-8, 0.1, 1, 0};
+    bfz_adamw hp{1e-4, 0.9, 0.95, 1e-8, 0.1, 1, 0, 0};
     const float* src[1] = {w};
     const float* src_odd[1] = {reinterpret_cast<const float*>(reinterpret_cast<const char*>(w) + 2)};
     uint8_t* d8[1] = {w8};
@@ -544,6 +657,15 @@ void run_error_paths() {
           "misaligned scale grid");
     CHECK(bfz_e4m3_encode(nullptr, c, 4, nullptr) == BFZ_EINVAL && bfz_e4m3_encode(a, c, -1, nullptr) == BFZ_EINVAL,
           "encode args");
+    bad = hp;
+    for (int64_t stride : {int64_t(-16384), int64_t(16383), int64_t(16386), (int64_t(1) << 26) + 4}) {
+        bad.state_stride = stride;
+        CHECK(adamw_fp8_step(a, a, a, a, c, s, q, &bad, nullptr) == BFZ_EINVAL &&
+                  std::strstr(bfz_last_error(), "state_stride"),
+              "bad state_stride %lld", (long long)stride);
+        CHECK(pack_shard_strided(plan, src, a, stride, nullptr) == BFZ_EINVAL, "bad dst_stride %lld",
+              (long long)stride);
+    }
     CHECK(std::strlen(bfz_last_error()) > 0, "message");
     std::free(a);
     std::free(c);
@@ -577,6 +699,9 @@ int main() {
         many.push_back(uniform(1, 140));
     }
     run_plan_case(many, 3);
+    // both state layouts, one weight and several segments
+    run_layout_case({2, 300, 200, 1, 129, 257}, 2);
+    run_layout_case(many, 3);
     if (g_failures) {
         std::fprintf(stderr, "%d checks failed\n", g_failures);
         return 1;

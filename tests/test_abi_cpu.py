@@ -119,6 +119,43 @@ def test_step_argument_errors_without_gpu():
         assert _call_step(ok, hp=hp) == bfz.BFZ_EINVAL, field
 
 
+@pytest.mark.parametrize("stride", [-16384, 1, 16383, 16386, 49150, (1 << 26) + 4, 1 << 40])
+def test_bad_state_stride_is_rejected_without_gpu(stride):
+    """state_stride: 0, or a multiple of 4 in [16384, 2^26] (tiles of
+    master / m / v may not overlap and must stay 16-byte aligned)."""
+    ok = [0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000]
+    hp = bfz.AdamW(lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1,
+                   state_stride=stride)
+    assert _call_step(ok, hp=hp) == bfz.BFZ_EINVAL
+    assert "state_stride" in bfz.lib().bfz_last_error().decode()
+    L = bfz.lib()
+    p = bfz.Plan([(1, 256, 256)], 1, 0, upload=False)
+    src = (C.c_void_p * 1)(0x10000)
+    assert L.pack_shard_strided(p.handle, C.cast(src, C.c_void_p), C.c_void_p(0x30000), stride,
+                                None) == bfz.BFZ_EINVAL
+    assert "dst_stride" in L.bfz_last_error().decode()
+    p.close()
+
+
+def test_good_state_stride_passes_the_checks():
+    """Valid strides get past their check: pack_shard_strided stops at the
+    plan (not uploaded: BFZ_ESTATE), and a step whose only fault is beta1 = 1
+    reports that, not the stride."""
+    L = bfz.lib()
+    p = bfz.Plan([(1, 256, 256)], 1, 0, upload=False)
+    src = (C.c_void_p * 1)(0x10000)
+    ok = [0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000]
+    for stride in (0, 16384, 49152, 1 << 26):
+        assert L.pack_shard_strided(p.handle, C.cast(src, C.c_void_p), C.c_void_p(0x30000),
+                                    stride or 16384, None) == bfz.BFZ_ESTATE
+        hp = bfz.AdamW(lr=1e-4, beta1=1.0, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1,
+                       state_stride=stride)
+        assert _call_step(ok, hp=hp) == bfz.BFZ_EINVAL
+        msg = L.bfz_last_error().decode()
+        assert "beta" in msg and "state_stride" not in msg, msg
+    p.close()
+
+
 def test_pack_unpack_errors_without_gpu():
     L = bfz.lib()
     p = bfz.Plan([(1, 256, 256), (1, 128, 128)], 2, 0, upload=False)

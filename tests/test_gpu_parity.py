@@ -44,11 +44,17 @@ def _check(gpu, ora, what):
 MODES = list(GpuWorkload.MODES)
 
 
+LAYOUTS = list(GpuWorkload.LAYOUTS)
+# the state layout bench.py times (one [master | m | v] block per tile)
+BENCH_LAYOUT = "interleaved"
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("mode", MODES)
-def test_tiny_every_step_every_slot(mode):
+def test_tiny_every_step_every_slot(mode, layout):
     w = WL.tiny()
-    _say("tiny: 256x384, 3 steps, seed", w.seed, "mode", mode)
-    g = GpuWorkload(w, mode=mode)
+    _say("tiny: 256x384, 3 steps, seed", w.seed, "mode", mode, "layout", layout)
+    g = GpuWorkload(w, mode=mode, layout=layout)
     g.load_state()
     slots = list(range(g.q))
     for k, t in enumerate(w.steps):
@@ -67,11 +73,12 @@ def test_tiny_every_step_every_slot(mode):
     assert np.array_equal(sc[0].cpu().numpy().reshape(E, 2, 3), osc)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("mode", MODES)
-def test_ragged_every_slot(mode):
+def test_ragged_every_slot(mode, layout):
     w = WL.ragged()
-    _say("ragged: 40 matrices, D=8 rank 3, seed", w.seed, "mode", mode)
-    g = GpuWorkload(w, mode=mode)
+    _say("ragged: 40 matrices, D=8 rank 3, seed", w.seed, "mode", mode, "layout", layout)
+    g = GpuWorkload(w, mode=mode, layout=layout)
     g.load_state()
     g.run_steps()
     slots = list(range(g.q))
@@ -100,8 +107,8 @@ def test_ragged_every_slot(mode):
 def test_full_size_sampled(name, mode):
     w = WL.BY_NAME[name]()
     _say(name, "full size,", len(w.dims), "weights, D =", w.D, "rank", w.rank, "seed", w.seed,
-         "mode", mode)
-    g = GpuWorkload(w, mode=mode)
+         "mode", mode, "layout", BENCH_LAYOUT)
+    g = GpuWorkload(w, mode=mode, layout=BENCH_LAYOUT)
     g.load_state()
     g.run_steps()
     slots = sample_slots(w)
@@ -137,8 +144,8 @@ def test_lone_rank_rowmajor_only_full_size():
     FP8 weights and scale grids -- checked at the sampled tiles, with the
     master / moments, against the oracle."""
     w = WL.large()
-    _say("large, row-major output only (lone rank), full size")
-    g = GpuWorkload(w, mode="fused_unpack")
+    _say("large, row-major output only (lone rank), full size, layout", BENCH_LAYOUT)
+    g = GpuWorkload(w, mode="fused_unpack", layout=BENCH_LAYOUT)
     g.tile_codes = False
     g.codes.fill_(0xAB)
     g.scale_inv.fill_(-7.0)
@@ -176,11 +183,14 @@ def _beyond_32bit():
 _BIG = {}
 
 
-@pytest.mark.parametrize("mode", MODES)
-def test_offsets_beyond_32_bits(mode):
+# each route once; the one-kernel step in the interleaved layout, whose
+# state offsets (slot * 49152 floats) pass 2^32 already at slot 87,382
+@pytest.mark.parametrize("mode,layout", [("unfused", "separate"), ("fused", "separate"),
+                                         ("fused_unpack", "interleaved")])
+def test_offsets_beyond_32_bits(mode, layout):
     w = _beyond_32bit()
-    _say("beyond 32-bit offsets:", w.description, "mode", mode)
-    g = GpuWorkload(w, mode=mode)
+    _say("beyond 32-bit offsets:", w.description, "mode", mode, "layout", layout)
+    g = GpuWorkload(w, mode=mode, layout=layout)
     assert g.q * 16384 > 2 ** 32
     g.load_state()
     g.run_steps()
@@ -332,8 +342,9 @@ def test_random_configurations(seed):
                 assert np.array_equal(dsc[k].cpu().numpy(), osc[k].reshape(-1)), k
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("pow2", [False, True])
-def test_many_weights_several_segments(pow2):
+def test_many_weights_several_segments(pow2, layout):
     """A rank that owns 70+ small ragged weights, starting and ending
     mid-weight: its slots span several launch segments (at most 64 weights
     each) in every route -- tile-major step, fused fold, one-kernel step
@@ -349,7 +360,7 @@ def test_many_weights_several_segments(pow2):
     assert tuple(table[0][1:4]) != (0, 0, 0)                         # starts inside a weight
     assert oracle.plan(dims, D, rank + 1)[2][0][0] == table[owned - 1][0]  # ends inside one
     _say("many weights: 250 ragged, D", D, "rank", rank, "owns", owned, "tiles of", len(touched),
-         "weights, pow2", pow2)
+         "weights, pow2", pow2, "layout", layout)
     host = {k: [rng.normal(0, s, d).astype(np.float32) for d in dims]
             for k, s in (("p", 0.02), ("g", 1e-3), ("m", 1e-4))}
     host["v"] = [np.square(rng.normal(0, 1e-3, d)).astype(np.float32) for d in dims]
@@ -369,8 +380,12 @@ def test_many_weights_several_segments(pow2):
     routes = ["unfused", "fused", "fused_unpack"] + (["fused_unpack_t"] if pow2 else [])
     for route in routes:
         st = {}
+        if layout == "interleaved":  # segments start at slot0 * 49152 floats of one buffer
+            state = torch.empty((q, 3, 16384), dtype=torch.float32, device="cuda")
+            st = {"p": state[:, 0], "m": state[:, 1], "v": state[:, 2]}
         for k in ("p", "m", "v"):
-            st[k] = torch.empty(q * 16384, dtype=torch.float32, device="cuda")
+            if layout == "separate":
+                st[k] = torch.empty(q * 16384, dtype=torch.float32, device="cuda")
             bfz.pack_shard(plan, dev[k], st[k])
         codes = torch.empty(q * 16384, dtype=torch.uint8, device="cuda")
         sc = torch.empty(q, dtype=torch.float32, device="cuda")
@@ -395,10 +410,11 @@ def test_many_weights_several_segments(pow2):
             bfz.fold_adamw_fp8_step_unpack_t(plan, dev["g"], st["p"], st["m"], st["v"], codes, sc,
                                              d8, dsc, dt, dts, h)
         torch.cuda.synchronize()
-        gpu = dict(master=st["p"].cpu().numpy(), m=st["m"].cpu().numpy(), v=st["v"].cpu().numpy(),
-                   codes=codes.cpu().numpy(), scale_inv=sc.cpu().numpy())
+        gpu = dict(master=st["p"].cpu().numpy().reshape(-1), m=st["m"].cpu().numpy().reshape(-1),
+                   v=st["v"].cpu().numpy().reshape(-1), codes=codes.cpu().numpy(),
+                   scale_inv=sc.cpu().numpy())
         rep = _check(gpu, dict(master=ora["p"], m=ora["m"], v=ora["v"], codes=codes_o,
-                               scale_inv=scale_o, near=near_o), f"many weights {route}")
+                               scale_inv=scale_o, near=near_o), f"many weights {route} {layout}")
         assert rep["exact"]
         for k in range(len(dims)):
             assert np.array_equal(d8[k].cpu().numpy(), o8[k].reshape(-1)), (route, k)

@@ -128,8 +128,9 @@ def test_transpose_quantized_weights():
         assert np.array_equal(ds[p].cpu().numpy(), ods[p].reshape(-1)), p
 
 
-@pytest.mark.parametrize("tile_codes", [True, False])
-def test_fused_step_with_transposed_copy(tile_codes):
+@pytest.mark.parametrize("tile_codes,layout", [(True, "separate"), (False, "separate"),
+                                               (True, "interleaved")])
+def test_fused_step_with_transposed_copy(tile_codes, layout):
     """fold_adamw_fp8_step_unpack_t over the steps of ten ragged matrices:
     master, moments, codes and scales, the row-major FP8 weights and the
     transposed copy all equal the oracle's power-of-two step followed by its
@@ -137,8 +138,9 @@ def test_fused_step_with_transposed_copy(tile_codes):
     when tile_codes is False: those buffers stay untouched)."""
     w = WL.ragged()
     w.dims = w.dims[:10]
-    _say("fused step + transposed copy: 10 ragged matrices, D=8 rank 3, tile codes", tile_codes)
-    g = GpuWorkload(w, mode="fused_unpack", pow2=True, transposed=True)
+    _say("fused step + transposed copy: 10 ragged matrices, D=8 rank 3, tile codes", tile_codes,
+         "layout", layout)
+    g = GpuWorkload(w, mode="fused_unpack", pow2=True, transposed=True, layout=layout)
     g.tile_codes = tile_codes
     g.codes.fill_(0xAB)
     g.scale_inv.fill_(-7.0)
@@ -184,8 +186,8 @@ def test_fused_transposed_copy_full_size_sampled():
     oracle -- state, codes, scales, row-major FP8 and the W^T block with its
     group scales (the oracle's transposed copy of that tile alone)."""
     w = WL.dense_llm()
-    _say("dense_llm full size, fused step + transposed copy, pow2")
-    g = GpuWorkload(w, mode="fused_unpack", pow2=True, transposed=True)
+    _say("dense_llm full size, fused step + transposed copy, pow2, interleaved state")
+    g = GpuWorkload(w, mode="fused_unpack", pow2=True, transposed=True, layout="interleaved")
     g.load_state()
     g.run_steps()
     slots = sample_slots(w, n_random=48)
