@@ -66,8 +66,15 @@ def log(*a):
 
 
 def kernel_sha():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 of kernels.hip's code: comments removed and whitespace runs
+    collapsed, so that a comment edit does not orphan the committed counter
+    summaries while any change to the code does."""
+    with open(KERNEL_SRC) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = " ".join(src.split())
+    return hashlib.sha256(src.encode()).hexdigest()
 
 
 def measured_traffic(kernel):

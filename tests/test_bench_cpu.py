@@ -36,3 +36,22 @@ def test_traffic_is_reported_only_for_the_profiled_kernel_source(tmp_path, monke
     assert bench.measured_traffic("step_kernel") is None
     monkeypatch.setitem(bench.TRAFFIC_FILES, "step_kernel", str(tmp_path / "missing.md"))
     assert bench.measured_traffic("step_kernel") is None
+
+
+def test_kernel_hash_follows_code_not_comments(tmp_path, monkeypatch):
+    """A comment or whitespace edit keeps the hash (the compiled kernels are
+    the same); any change to the code changes it."""
+    src = open(bench.KERNEL_SRC).read()
+    base = bench.kernel_sha()
+    variants = {"comment": src.replace("namespace bfz {", "namespace bfz {  // a note\n/* block\n note */", 1),
+                "spaces": src.replace("\n", "\n   \n", 5),
+                "code": src.replace("kStepLdsBytes = 96 * 1024", "kStepLdsBytes = 95 * 1024", 1)}
+    assert variants["code"] != src
+    got = {}
+    for name, text in variants.items():
+        f = tmp_path / f"{name}.hip"
+        f.write_text(text)
+        monkeypatch.setattr(bench, "KERNEL_SRC", str(f))
+        got[name] = bench.kernel_sha()
+    assert got["comment"] == base and got["spaces"] == base and got["code"] != base
+
