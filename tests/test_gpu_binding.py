@@ -1,0 +1,93 @@
+"""The binding's state-layout marshalling on the GPU: master / m / v as
+contiguous tensors or as (tiles, 16384) views of one (q, 3, 16384) tensor;
+the stride each call passes in bfz_adamw.state_stride is the views' row
+stride, and inconsistent layouts are refused before any kernel runs."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import blockwise_fp8_zero_amd as bfz
+
+pytestmark = pytest.mark.gpu
+
+HP = dict(lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+
+
+def _say(*a):
+    print("[gpu-binding]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _bufs(q):
+    f32 = dict(dtype=torch.float32, device="cuda")
+    g = torch.randn(q * 16384, **f32) * 1e-3
+    codes = torch.empty(q * 16384, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(q, **f32)
+    return g, codes, sc
+
+
+def test_mismatched_state_strides_are_refused():
+    q = 3
+    _say("state-stride checks, q =", q)
+    g, codes, sc = _bufs(q)
+    state = torch.zeros(q, 3, 16384, dtype=torch.float32, device="cuda")
+    flat = torch.zeros(q * 16384, dtype=torch.float32, device="cuda")
+    hp = bfz.AdamW(step=1, **HP)
+    with pytest.raises(ValueError, match="different tile strides"):
+        bfz.adamw_fp8_step(state[:, 0], g, flat, state[:, 2], codes, sc, hp)
+    hp_bad = bfz.AdamW(step=1, state_stride=16384, **HP)
+    with pytest.raises(ValueError, match="disagrees"):
+        bfz.adamw_fp8_step(state[:, 0], g, state[:, 1], state[:, 2], codes, sc, hp_bad)
+    gappy = torch.zeros(q, 2 * 16384, dtype=torch.float32, device="cuda")[:, ::2]
+    with pytest.raises(TypeError):  # (q, 16384) but its elements are not contiguous within a tile
+        bfz.adamw_fp8_step(gappy, g, state[:, 1], state[:, 2], codes, sc, hp)
+    with pytest.raises(ValueError, match="tiles"):
+        bfz.adamw_fp8_step(state[:2, 0], g, state[:2, 1], state[:2, 2], codes, sc, hp, n_tiles=3)
+    torch.cuda.synchronize()
+    assert not state.any()  # nothing ran
+
+
+def test_caller_hp_is_not_modified_and_layouts_agree():
+    """The same step through contiguous arrays and through interleaved views
+    gives bit-identical results; the caller's AdamW struct keeps
+    state_stride 0 (the binding passes a copy)."""
+    q = 5
+    _say("layout agreement through the binding, q =", q)
+    torch.manual_seed(3)
+    g, codes_a, sc_a = _bufs(q)
+    codes_b = torch.empty_like(codes_a)
+    sc_b = torch.empty_like(sc_a)
+    p0 = torch.randn(q, 16384, device="cuda") * 0.02
+    m0 = torch.randn(q, 16384, device="cuda") * 1e-4
+    v0 = torch.rand(q, 16384, device="cuda") * 1e-6
+    sep = [x.clone().reshape(-1) for x in (p0, m0, v0)]
+    state = torch.stack([p0, m0, v0], dim=1).contiguous()
+    hp = bfz.AdamW(step=7, **HP)
+    bfz.adamw_fp8_step(*sep[:1], g, *sep[1:], codes_a, sc_a, hp)
+    bfz.adamw_fp8_step(state[:, 0], g, state[:, 1], state[:, 2], codes_b, sc_b, hp)
+    torch.cuda.synchronize()
+    assert hp.state_stride == 0
+    for k in range(3):
+        assert torch.equal(sep[k].view(torch.int32), state[:, k].reshape(-1).view(torch.int32)), k
+    assert torch.equal(codes_a, codes_b) and torch.equal(sc_a, sc_b)
+    assert not np.array_equal(sep[0].cpu().numpy(), p0.reshape(-1).cpu().numpy())  # it did step
+
+
+def test_single_tile_and_empty_views():
+    """q = 1: a (1, 16384) view has no stride of its own and is accepted
+    next to contiguous tensors; n_tiles = 0 is a no-op."""
+    _say("single-tile views and n_tiles = 0")
+    g, codes, sc = _bufs(1)
+    state = torch.zeros(1, 3, 16384, dtype=torch.float32, device="cuda")
+    state[:, 0] = 0.5
+    flat = torch.zeros(16384, dtype=torch.float32, device="cuda")
+    hp = bfz.AdamW(step=1, **HP)
+    bfz.adamw_fp8_step(state[:, 0], g, flat, state[:, 2], codes, sc, hp)
+    torch.cuda.synchronize()
+    assert float(sc[0]) > 0 and flat.abs().sum() > 0
+    before = state.clone()
+    bfz.adamw_fp8_step(state[:, 0], g, state[:, 1], state[:, 2], codes, sc, hp, n_tiles=0)
+    torch.cuda.synchronize()
+    assert torch.equal(before, state)
