@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "bfz_internal.h"
 
@@ -126,65 +127,129 @@ constexpr int kStepWaves = kStepThreads / 64;
 constexpr int kStepVec = kTileElems / 4 / kStepThreads;  // float4 per thread per array
 constexpr int kStepLdsBytes = 96 * 1024;                 // > half of the 160 KiB per CU
 
+// A gradient source has two phases per float4 k: load(k, spare) issues
+// the memory reads, finish(k, raw) turns what they returned into the
+// float4.  step_tile issues every load of the tile before finishing any, so
+// the lane shuffles of misaligned rows no longer make the wave wait for all
+// its outstanding reads once per float4.  A lane with nothing to read
+// (outside the weight's edge, or a padding slot) reads `spare` instead -- a
+// 16-byte block of the same tile that the wave reads anyway -- and finish()
+// discards it: lane-divergent branches around those loads made the compiler
+// wait for every outstanding read where they joined.
+
 // Gradient of a tile already folded into the tile-major shard.
 struct TileMajorGrad {
     const f32x4* tile;
-    __device__ __forceinline__ f32x4 operator()(int k) const {
+    typedef f32x4 Raw;
+    __device__ __forceinline__ Raw load(int k, const f32x4*) const {
         return load_stream(tile + k * kStepThreads + threadIdx.x);
     }
+    __device__ __forceinline__ f32x4 finish(int, const Raw& r) const { return r; }
 };
 
 // Gradient read straight from the weight's row-major tensor (the fold done
 // on the fly): row 32 k + thread / 32, four columns from 4 (thread % 32).
 // Outside the weight's edge, and in padding slots (origin == nullptr), the
-// gradient is +0.0 -- exactly what the fold would have stored there.
+// gradient is +0.0 -- exactly what the fold would have stored there.  Two
+// sources, chosen per tile (uniform over the workgroup, so neither load
+// phase holds a branch): RowMajorGrad for rows on 16-byte boundaries
+// (W % 4 == 0, 16-byte aligned weight) and padding slots,
+// ShiftedRowMajorGrad for rows that start off a 16-byte boundary.
 struct RowMajorGrad {
-    const float* origin;  // the tile's element (0, 0) in its weight
+    const float* origin;  // the tile's element (0, 0) in its weight; nullptr: padding
     int32_t ld;
     int16_t rows, cols;
-    bool vec;             // W % 4 == 0 and the weight is 16-byte aligned
-    __device__ __forceinline__ f32x4 operator()(int k) const {
+    typedef f32x4 Raw;
+    __device__ __forceinline__ bool lane_ok(int k, int c) const {
+        return origin != nullptr && k * 32 + (int)(threadIdx.x >> 5) < rows && c < cols;
+    }
+    // W % 4 == 0 makes the tile's valid width a multiple of 4: each float4
+    // lies wholly inside or wholly outside it
+    __device__ __forceinline__ Raw load(int k, const f32x4* spare) const {
         const int r = k * 32 + (threadIdx.x >> 5), c = 4 * (threadIdx.x & 31);
-        f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (origin == nullptr) return x;
-        if (vec) {
-            if (r >= rows) return x;
-            const float* q = origin + (int64_t)r * ld + c;
-            if (c + 4 <= cols) return load_stream(reinterpret_cast<const f32x4*>(q));
-#pragma unroll
-            for (int l = 0; l < 4; ++l)
-                if (c + l < cols) x[l] = q[l];
-            return x;
-        }
-        // A row that starts a floats past a 16-byte boundary: lane l loads the
-        // aligned block holding row elements c - a .. c - a + 3 and takes the
-        // a elements it lacks from its right neighbour's block (the row's last
-        // lane loads one more block).  A block is read only if it holds an
-        // element of the row's valid part; an aligned 16-byte block never
-        // crosses a page, so every read stays in mapped memory.  Both rows of
-        // a wave run the shuffle unconditionally (32-lane segments).
+        const f32x4* q = reinterpret_cast<const f32x4*>(origin + (int64_t)r * ld + c);
+        return load_stream(lane_ok(k, c) ? q : spare);
+    }
+    __device__ __forceinline__ f32x4 finish(int k, const Raw& x) const {
+        const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        return lane_ok(k, 4 * (threadIdx.x & 31)) ? x : zero;
+    }
+};
+
+// A row that starts a floats past a 16-byte boundary (a = 1..3: odd W or an
+// offset weight): lane l loads the aligned block holding row elements
+// c - a .. c - a + 3 and takes the a elements it lacks from its right
+// neighbour's block (a 32-lane shuffle); the row's last lane also loads the
+// block after.  A block is read only if it holds an element of the row's
+// valid part; an aligned 16-byte block never crosses a page, so every read
+// stays in mapped memory.
+struct ShiftedRowMajorGrad {
+    const float* origin;
+    int32_t ld;
+    int16_t rows, cols;
+    struct Raw {
+        f32x4 f, g;  // the block under the lane, and the one after (last lane)
+    };
+    __device__ __forceinline__ Raw load(int k, const f32x4* spare) const {
+        const int r = k * 32 + (threadIdx.x >> 5), c = 4 * (threadIdx.x & 31);
         const bool row_ok = r < rows;
         const float* row = origin + (int64_t)(row_ok ? r : 0) * ld;
         const int a = (int)((reinterpret_cast<uintptr_t>(row) >> 2) & 3u);
         const f32x4* blk = reinterpret_cast<const f32x4*>(row - a) + (c >> 2);
         const bool last = (threadIdx.x & 31) == 31;
-        f32x4 f = {0.0f, 0.0f, 0.0f, 0.0f}, g = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (row_ok && c - a < cols) f = load_stream(blk);
-        if (row_ok && last && a > 0 && kTileDim - a < cols) g = load_stream(blk + 1);
+        Raw x;
+        x.f = load_stream(row_ok && c - a < cols ? blk : spare);
+        // the extra block is the last lane's alone: a masked load (giving
+        // every lane the spare read instead measured 3% slower on ragged
+        // weights)
+        x.g = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (row_ok && last && a > 0 && kTileDim - a < cols) x.g = load_stream(blk + 1);
+        return x;
+    }
+    // Both rows of a wave run the shuffle unconditionally (32-lane segments).
+    __device__ __forceinline__ f32x4 finish(int k, const Raw& x) const {
+        const int r = k * 32 + (threadIdx.x >> 5), c = 4 * (threadIdx.x & 31);
+        const bool row_ok = r < rows;
+        const float* row = origin + (int64_t)(row_ok ? r : 0) * ld;
+        const int a = (int)((reinterpret_cast<uintptr_t>(row) >> 2) & 3u);
+        const bool last = (threadIdx.x & 31) == 31;
+        // g's last float is never selected below (a <= 3); keep it live to
+        // here, or its register is reused while the load into it is still
+        // in flight, which makes the wave wait right after issuing it
+        __asm__ volatile("" : : "v"(x.g[3]));
+        const f32x4 f = x.f;
         f32x4 n;
 #pragma unroll
         for (int l = 0; l < 4; ++l) n[l] = __shfl_down(f[l], 1, 32);
-        if (last) n = g;
-        x[0] = a == 0 ? f[0] : a == 1 ? f[1] : a == 2 ? f[2] : f[3];
-        x[1] = a == 0 ? f[1] : a == 1 ? f[2] : a == 2 ? f[3] : n[0];
-        x[2] = a == 0 ? f[2] : a == 1 ? f[3] : a == 2 ? n[0] : n[1];
-        x[3] = a == 0 ? f[3] : a == 1 ? n[0] : a == 2 ? n[1] : n[2];
+        if (last) n = x.g;
+        f32x4 y;
+        y[0] = a == 0 ? f[0] : a == 1 ? f[1] : a == 2 ? f[2] : f[3];
+        y[1] = a == 0 ? f[1] : a == 1 ? f[2] : a == 2 ? f[3] : n[0];
+        y[2] = a == 0 ? f[2] : a == 1 ? f[3] : a == 2 ? n[0] : n[1];
+        y[3] = a == 0 ? f[3] : a == 1 ? n[0] : a == 2 ? n[1] : n[2];
 #pragma unroll
         for (int l = 0; l < 4; ++l)
-            if (!row_ok || c + l >= cols) x[l] = 0.0f;
-        return x;
+            if (!row_ok || c + l >= cols) y[l] = 0.0f;
+        return y;
     }
 };
+
+// The gradient source of slot entry t in the launch's weights: calls
+// f(source) with RowMajorGrad or ShiftedRowMajorGrad (padding slots take
+// the former with no origin).
+template <class F>
+__device__ __forceinline__ void with_row_major_grad(const TileEntry& t, const PackArgs& grads,
+                                                    F&& f) {
+    if (t.local < 0) {
+        f(RowMajorGrad{nullptr, t.ld, t.valid_rows, t.valid_cols});
+        return;
+    }
+    const float* w = grads.src[t.local];
+    if (((t.ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(w) & 15u) == 0))
+        f(RowMajorGrad{w + t.base, t.ld, t.valid_rows, t.valid_cols});
+    else
+        f(ShiftedRowMajorGrad{w + t.base, t.ld, t.valid_rows, t.valid_cols});
+}
 
 // Where a tile's codes and scale go besides the tile-major shard: straight
 // into the row-major FP8 weight and its scale grid (the unfold done in the
@@ -229,14 +294,17 @@ __device__ __forceinline__ float step_tile(int64_t tile, float* __restrict__ mas
     f32x4* V = reinterpret_cast<f32x4*>(mom2) + sbase;
 
     f32x4 p[kStepVec], g[kStepVec], m[kStepVec], v[kStepVec];
+    typename GradFn::Raw graw[kStepVec];
 #pragma unroll
     for (int k = 0; k < kStepVec; ++k) {
         const int i = k * kStepThreads + threadIdx.x;
         p[k] = load_stream(P + i);
-        g[k] = grad_at(k);
+        graw[k] = grad_at.load(k, P + i);
         m[k] = load_stream(M + i);
         v[k] = load_stream(V + i);
     }
+#pragma unroll
+    for (int k = 0; k < kStepVec; ++k) g[k] = grad_at.finish(k, graw[k]);
     float amax = 0.0f;
 #pragma unroll
     for (int k = 0; k < kStepVec; ++k) {
@@ -304,13 +372,9 @@ __global__ __launch_bounds__(kStepThreads) void fold_step_kernel(
     extern __shared__ float wave_amax[];
     const int64_t slot = xcd_tile(blockIdx.x, n_slots);
     const TileEntry t = entries[slot];
-    RowMajorGrad g{nullptr, t.ld, t.valid_rows, t.valid_cols, false};
-    if (t.local >= 0) {
-        const float* w = grads.src[t.local];
-        g.origin = w + t.base;
-        g.vec = ((t.ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(w) & 15u) == 0);
-    }
-    step_tile(slot, master, mom1, mom2, codes, scale_inv, s, g, wave_amax);
+    with_row_major_grad(t, grads, [&](const auto& g) {
+        step_tile(slot, master, mom1, mom2, codes, scale_inv, s, g, wave_amax);
+    });
 }
 
 // Fold, step and unfold in one pass: as fold_step_kernel, and each owned
@@ -323,18 +387,16 @@ __global__ __launch_bounds__(kStepThreads) void fold_step_unfold_kernel(
     extern __shared__ float wave_amax[];
     const int64_t slot = xcd_tile(blockIdx.x, n_slots);
     const TileEntry t = entries[slot];
-    RowMajorGrad g{nullptr, t.ld, t.valid_rows, t.valid_cols, false};
     RowMajorCodes out{nullptr, nullptr, t.ld, t.valid_rows, t.valid_cols, false};
     if (t.local >= 0) {
-        const float* w = grads.src[t.local];
-        g.origin = w + t.base;
-        g.vec = ((t.ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(w) & 15u) == 0);
         uint8_t* d = outs.codes[t.local];
         out.origin = d + t.base;
         out.scale_cell = outs.scale[t.local] + t.scale_index;
         out.vec = ((t.ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(d) & 3u) == 0);
     }
-    step_tile(slot, master, mom1, mom2, codes, scale_inv, s, g, wave_amax, out);
+    with_row_major_grad(t, grads, [&](const auto& g) {
+        step_tile(slot, master, mom1, mom2, codes, scale_inv, s, g, wave_amax, out);
+    });
 }
 
 // Fold: one 1024-thread workgroup per slot, the step kernels' thread
@@ -349,17 +411,17 @@ __global__ __launch_bounds__(kStepThreads) void pack_kernel(const TileEntry* __r
     const int64_t slot = xcd_tile(blockIdx.x, gridDim.x);
     const TileEntry t = entries[slot];
     f32x4* out = reinterpret_cast<f32x4*>(dst + slot * dst_stride);
-    RowMajorGrad src{nullptr, t.ld, t.valid_rows, t.valid_cols, false};
-    if (t.local >= 0) {
-        const float* w = args.src[t.local];
-        src.origin = w + t.base;
-        src.vec = ((t.ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(w) & 15u) == 0);
-    }
-    f32x4 x[kStepVec];
+    // a lane with nothing to read loads its own (not yet written) output block
+    with_row_major_grad(t, args, [&](const auto& src) {
+        typename std::decay_t<decltype(src)>::Raw raw[kStepVec];
 #pragma unroll
-    for (int k = 0; k < kStepVec; ++k) x[k] = src(k);
+        for (int k = 0; k < kStepVec; ++k) raw[k] = src.load(k, out + k * kStepThreads + threadIdx.x);
+        f32x4 x[kStepVec];
 #pragma unroll
-    for (int k = 0; k < kStepVec; ++k) store_stream(out + k * kStepThreads + threadIdx.x, x[k]);
+        for (int k = 0; k < kStepVec; ++k) x[k] = src.finish(k, raw[k]);
+#pragma unroll
+        for (int k = 0; k < kStepVec; ++k) store_stream(out + k * kStepThreads + threadIdx.x, x[k]);
+    });
 }
 
 // Unfold of codes and scales: one workgroup per owned slot, XCD-contiguous
@@ -698,19 +760,18 @@ __global__ __launch_bounds__(kStepThreads) void fold_step_unfold_t_kernel(
     uint32_t* tile_t = tile_rm + kTileElems / 4;                   // 16 KiB, codes by W^T rows
     const int64_t slot = xcd_tile(blockIdx.x, n_slots);
     const TileEntry t = entries[slot];
-    RowMajorGrad g{nullptr, t.ld, t.valid_rows, t.valid_cols, false};
     StagedCodes out{RowMajorCodes{nullptr, nullptr, t.ld, t.valid_rows, t.valid_cols, false}, nullptr,
                     tile_rm};
     if (t.local >= 0) {
-        const float* w = grads.src[t.local];
-        g.origin = w + t.base;
-        g.vec = ((t.ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(w) & 15u) == 0);
         uint8_t* d = outs.codes[t.local];
         out.rm.origin = d + t.base;
         out.rm.vec = ((t.ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(d) & 3u) == 0);
         out.scale_cell = outs.scale[t.local] + t.scale_index;
     }
-    const float scale = step_tile(slot, master, mom1, mom2, codes, scale_inv, s, g, wave_amax, out);
+    float scale = 0.0f;
+    with_row_major_grad(t, grads, [&](const auto& g) {
+        scale = step_tile(slot, master, mom1, mom2, codes, scale_inv, s, g, wave_amax, out);
+    });
     __syncthreads();
     {
         const int rq = threadIdx.x & 31, bc = threadIdx.x >> 5;
