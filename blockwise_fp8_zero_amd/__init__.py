@@ -232,6 +232,19 @@ def pack_shard(plan: Plan, srcs, dst, stream=None):
                                         _stream(stream)))
 
 
+def pack_shard_strided(plan: Plan, srcs, dst, dst_stride, stream=None):
+    """pack_shard into a flat float32 buffer whose slot s starts at
+    s * dst_stride floats (dst must hold (q - 1) * dst_stride + 16384
+    floats); pack_shard does the same given a (q, 16384) view."""
+    import torch
+    q = plan.shard_tiles
+    need = (q - 1) * int(dst_stride) + TILE_ELEMS if q else 0
+    arr = _ptr_array(srcs, torch.float32, "srcs", len(plan.dims))
+    d = _dev(dst, torch.float32, "dst", need)
+    _check(lib().pack_shard_strided(plan.handle, C.cast(arr, C.c_void_p), d, int(dst_stride),
+                                    _stream(stream)))
+
+
 def adamw_fp8_step(master, grad, m, v, codes, scale_inv, hp, n_tiles=None, stream=None):
     """Fused AdamW + per-tile E4M3 requant over n_tiles whole tiles (default:
     all of master).  hp: AdamW, or a dict of its fields.  master / m / v:

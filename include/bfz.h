@@ -21,7 +21,10 @@
  *
  * Conventions shared by every call:
  *   - A tile is 16384 contiguous elements: 128 rows of 128, row-major.
- *     A shard is q tiles back to back (q = bfz_plan_shard_tiles).
+ *     A shard is q tiles back to back (q = bfz_plan_shard_tiles), except
+ *     the FP32 optimizer state (master, m, v), whose tiles may sit a stride
+ *     apart (bfz_adamw.state_stride; e.g. one [master | m | v] block per
+ *     tile) -- same values, same order, other addresses.
  *   - Device pointers are caller-owned (the library never frees them); the
  *     library allocates only the plan's small device table, in
  *     bfz_plan_upload, freed by bfz_plan_destroy.

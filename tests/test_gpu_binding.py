@@ -91,3 +91,29 @@ def test_single_tile_and_empty_views():
     bfz.adamw_fp8_step(state[:, 0], g, state[:, 1], state[:, 2], codes, sc, hp, n_tiles=0)
     torch.cuda.synchronize()
     assert torch.equal(before, state)
+
+
+def test_pack_shard_strided_flat_buffer_equals_views():
+    """pack_shard_strided into a flat buffer at stride 49152 gives, bit for
+    bit, the tiles pack_shard writes into a (q, 16384) view of the same
+    layout and into a contiguous shard; the gaps are not written."""
+    dims = [(1, 300, 200), (2, 129, 257)]
+    plan = bfz.Plan(dims, 2, 1)
+    q = plan.shard_tiles
+    _say("pack_shard_strided, dims", dims, "q =", q)
+    torch.manual_seed(5)
+    src = [torch.randn(E * H * W, device="cuda") for E, H, W in dims]
+    flat = torch.full((q * 49152,), -1.0, device="cuda")
+    bfz.pack_shard_strided(plan, src, flat, 49152)
+    view = torch.full((q, 3, 16384), -1.0, device="cuda")
+    bfz.pack_shard(plan, src, view[:, 1])
+    ref = torch.empty(q * 16384, device="cuda")
+    bfz.pack_shard(plan, src, ref)
+    torch.cuda.synchronize()
+    tiles = flat.view(q, 3, 16384)[:, 0]
+    assert torch.equal(tiles.reshape(-1).view(torch.int32), ref.view(torch.int32))
+    assert torch.equal(view[:, 1].reshape(-1).view(torch.int32), ref.view(torch.int32))
+    assert (flat.view(q, 3, 16384)[:, 1:] == -1.0).all() and (view[:, 0::2] == -1.0).all()
+    with pytest.raises(ValueError):  # too short for q tiles at this stride
+        bfz.pack_shard_strided(plan, src, flat[: (q - 1) * 49152], 49152)
+
