@@ -699,6 +699,10 @@ int main() {
         many.push_back(uniform(1, 140));
     }
     run_plan_case(many, 3);
+    // tall weights over several ranks: ownership cut inside tile columns,
+    // tile-row counts that are not multiples of 4
+    run_plan_case({1, 1100, 300, 2, 700, 520}, 3);
+    run_plan_case({1, 2000, 130, 1, 129, 4000}, 5);
     // both state layouts, one weight and several segments
     run_layout_case({2, 300, 200, 1, 129, 257}, 2);
     run_layout_case(many, 3);

@@ -40,6 +40,11 @@ CASES = [
     ([(2, 300, 129), (1, 77, 513), (1, 1, 1)], 1, 0),
     ([(3, 129, 130), (1, 128, 1000)], 3, 1),
     ([(1, 640, 48)] * 140, 2, 1),  # rank owns 70 weights: several launch segments
+    # tall weights: ownership cut inside tile columns, tile-row counts that
+    # are not multiples of 4
+    ([(1, 1100, 300), (2, 700, 520)], 3, 1),
+    ([(1, 2000, 130), (1, 129, 4000)], 5, 2),
+    ([(1, 1024, 256)], 2, 1),
 ]
 
 
