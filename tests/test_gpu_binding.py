@@ -117,3 +117,30 @@ def test_pack_shard_strided_flat_buffer_equals_views():
     with pytest.raises(ValueError):  # too short for q tiles at this stride
         bfz.pack_shard_strided(plan, src, flat[: (q - 1) * 49152], 49152)
 
+
+
+@pytest.mark.parametrize("mode", ["unfused", "fused", "fused_unpack"])
+def test_gapped_state_stride(mode):
+    """A state layout with gaps -- four tile slots per block, the fourth
+    unused (state_stride 65536) -- through every step route on ragged
+    weights that span several tiles: bit-identical to three separate
+    arrays, and the gap slots are never written."""
+    from synth import workloads as WL
+    from tests.gpu_run import GpuWorkload
+    w = WL.ragged()
+    w.dims = w.dims[:6]
+    _say("gapped state stride 65536, 6 ragged matrices, mode", mode)
+    ref = GpuWorkload(w, mode=mode, layout="separate")
+    gap = GpuWorkload(w, mode=mode, layout="separate")
+    q = gap.q
+    block = torch.full((q, 4, 16384), 7.0, dtype=torch.float32, device="cuda")
+    gap.master, gap.m, gap.v = block[:, 0], block[:, 1], block[:, 2]
+    for g in (ref, gap):
+        g.load_state()
+        g.run_steps()
+    torch.cuda.synchronize()
+    a = ref.tiles(list(range(q)))
+    b = gap.tiles(list(range(q)))
+    for k in a:
+        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+    assert (block[:, 3] == 7.0).all()
