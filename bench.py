@@ -30,8 +30,10 @@ step.  roofline = the step kernel's algorithmic HBM bytes per launch
 (29 B per element + 4 B per tile, plus 1 B per element + 4 B per tile for
 the row-major codes and scales in the one-kernel path; gradient reads and
 row-major writes count valid elements) over its mean launch time, measured
-with HIP events on the stream the kernels run on.  cpu_baseline = the C oracle on a bounded sample of the
-same workload, on the host's cores.
+with HIP events on the stream the kernels run on.  pack / unpack = the fold
+and the unfold timed the same way where they run as passes of their own
+(unfused / fused routes).  cpu_baseline = the C oracle on a bounded sample
+of the same workload, on the host's cores.
 """
 import argparse
 import hashlib
@@ -294,8 +296,14 @@ def main():
     t_next = w.measured_step
 
     def one_step(t, ev=None):
+        # ev: HIP events around the step kernel (0, 1), the fold (2, 3) and
+        # the unfold (4, 5), recorded on the stream the kernels run on
         if args.path == "unfused":
+            if ev is not None:
+                ev[2].record(stream)
             g.pack_grads()
+            if ev is not None:
+                ev[3].record(stream)
         if ev is not None:
             ev[0].record(stream)
         if args.path == "unfused":
@@ -307,7 +315,11 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         if not one_kernel:
+            if ev is not None:
+                ev[4].record(stream)
             g.unpack(fp8, sc)
+            if ev is not None:
+                ev[5].record(stream)
 
     g.tile_codes = not lone
     for _ in range(args.warmup):
@@ -315,8 +327,7 @@ def main():
         t_next += 1
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(6)) for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -327,7 +338,11 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    step_kernel_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps
+    step_kernel_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    pack_ms = (sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+               if args.path == "unfused" else None)
+    unpack_ms = (sum(e[4].elapsed_time(e[5]) for e in evs) / args.steps
+                 if not one_kernel else None)
     ms_per_step = total_ms / args.steps
 
     elems = g.q * bfz.TILE_ELEMS
@@ -356,6 +371,12 @@ def main():
     transpose = None
     if not args.skip_transpose:
         transpose = time_transpose(g, t_next, args.steps, stream)
+
+    def pass_stats(ms, algo):
+        if ms is None:
+            return None
+        gbps = algo / (ms * 1e-3) / 1e9
+        return {"ms": ms, "algorithmic_bytes": algo, "GBps": gbps, "frac": gbps / HBM_PEAK_GBPS}
 
     out = {
         "metric": METRIC,
@@ -405,6 +426,12 @@ def main():
         },
         "cpu_baseline": None,
         "transpose_pow2": transpose,
+        # the fold and the unfold as passes of their own (unfused / fused
+        # routes): fold reads the valid gradient elements and writes whole
+        # tiles; unfold reads the owned tiles' codes and scales and writes
+        # the valid codes and the scale-grid cells
+        "pack": pass_stats(pack_ms, 4 * valid + 4 * elems),
+        "unpack": pass_stats(unpack_ms, g.owned * bfz.TILE_ELEMS + valid + 8 * g.owned),
     }
     if not args.skip_cpu_baseline:
         log("cpu baseline (oracle) ...")
