@@ -14,6 +14,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libbfz.so")
 TILE = 128
 TILE_ELEMS = TILE * TILE
+# the interleaved state layout (BFZ_STATE_STRIDE_INTERLEAVED): one
+# [master | m | v] block per tile; with state = torch.zeros(q, STATE_STRIDE),
+# pass state[:, :16384], state[:, 16384:32768] and state[:, 32768:] as
+# master, m and v
+STATE_STRIDE = 49152
 
 BFZ_OK, BFZ_EINVAL, BFZ_EALIGN, BFZ_EHIP, BFZ_ESTATE = 0, -1, -2, -3, -4
 

@@ -47,6 +47,9 @@ extern "C" {
 
 #define BFZ_TILE_DIM 128
 #define BFZ_TILE_ELEMS 16384
+/* The interleaved state layout's tile stride, in floats (see
+ * bfz_adamw.state_stride): one [master | m | v] block per tile. */
+#define BFZ_STATE_STRIDE_INTERLEAVED 49152
 
 #define BFZ_OK 0
 #define BFZ_EINVAL (-1) /* null pointer, bad size or shape, bad hyper-parameter */
@@ -69,12 +72,14 @@ typedef struct bfz_plan bfz_plan;
  * state_stride: floats from tile s to tile s + 1 in each of master, m and
  * v (the FP32 state of the shard).  0 means 16384: three separate
  * tile-major arrays.  Otherwise a multiple of 4 in [16384, 2^26]; the
- * three arrays' tiles must not overlap one another.  49152 with
- * m = master + 16384 and v = master + 32768 is the interleaved layout: one
- * contiguous 192 KiB block [master | m | v] per tile, so each tile's
- * updated state leaves as a single write stream (on MI355X about 7% more
- * HBM throughput than three separate arrays).  The gradient, codes and
- * scale_inv keep their tile-major layout whatever this value. */
+ * three arrays' tiles must not overlap one another.  With m = master +
+ * 16384 and v = master + 32768 the state is interleaved: one contiguous
+ * 192 KiB block [master | m | v] per tile, so each tile's updated state
+ * leaves as a single write stream (on MI355X 4-7% faster than three
+ * separate arrays); BFZ_STATE_STRIDE_INTERLEAVED is that stride, 49152.
+ * Larger strides leave gaps between the blocks, which are never read or
+ * written.  The gradient, codes and scale_inv keep their tile-major layout
+ * whatever this value. */
 typedef struct {
     double lr, beta1, beta2, eps, weight_decay;
     int64_t step;

@@ -35,9 +35,9 @@ class GpuWorkload:
         transposed (fused_unpack with pow2 only): fold_adamw_fp8_step_unpack_t,
         which also writes W^T and its group scales (self.out_t / self.out_t_scale).
         layout: the FP32 state -- "separate": master, m, v are three
-        tile-major arrays; "interleaved": one (q, 3, 16384) tensor, each
-        tile's [master | m | v] contiguous, passed as its three (q, 16384)
-        views (state_stride 49152)."""
+        tile-major arrays; "interleaved": one (q, bfz.STATE_STRIDE) tensor,
+        each tile's [master | m | v] contiguous, passed as its three
+        (q, 16384) column views."""
         assert mode in self.MODES, mode
         assert layout in self.LAYOUTS, layout
         self.layout = layout
@@ -58,8 +58,9 @@ class GpuWorkload:
         n = self.q * TILE_ELEMS
         kw = dict(device=self.device)
         if layout == "interleaved":
-            self.state = torch.empty((self.q, 3, TILE_ELEMS), dtype=torch.float32, **kw)
-            self.master, self.m, self.v = self.state[:, 0], self.state[:, 1], self.state[:, 2]
+            self.state = torch.empty((self.q, bfz.STATE_STRIDE), dtype=torch.float32, **kw)
+            self.master, self.m, self.v = (self.state[:, k * TILE_ELEMS:(k + 1) * TILE_ELEMS]
+                                           for k in range(3))
         else:
             self.master = torch.empty(n, dtype=torch.float32, **kw)
             self.m = torch.empty(n, dtype=torch.float32, **kw)
