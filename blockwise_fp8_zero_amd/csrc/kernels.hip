@@ -129,13 +129,14 @@ constexpr int kStepLdsBytes = 96 * 1024;                 // > half of the 160 Ki
 
 // A gradient source has two phases per float4 k: load(k, spare) issues
 // the memory reads, finish(k, raw) turns what they returned into the
-// float4.  step_tile issues every load of the tile before finishing any, so
-// the lane shuffles of misaligned rows no longer make the wave wait for all
-// its outstanding reads once per float4.  A lane with nothing to read
-// (outside the weight's edge, or a padding slot) reads `spare` instead -- a
-// 16-byte block of the same tile that the wave reads anyway -- and finish()
-// discards it: lane-divergent branches around those loads made the compiler
-// wait for every outstanding read where they joined.
+// float4.  step_tile places every load of the tile before the first finish
+// (the compiler then schedules them), so the lane shuffles of misaligned
+// rows do not make the wave wait for all its outstanding reads once per
+// float4.  A lane with nothing to read (outside the weight's edge, or a
+// padding slot) reads `spare` instead -- a 16-byte block of the same tile
+// that the wave reads anyway -- and finish() discards it: lane-divergent
+// branches around those loads would make the compiler wait for every
+// outstanding read where they join.
 
 // Gradient of a tile already folded into the tile-major shard.
 struct TileMajorGrad {
