@@ -642,3 +642,35 @@ def test_runs_on_the_callers_stream(mode):
         assert np.array_equal(ta[k].view(np.uint8), tb[k].view(np.uint8)), k
     for a, b in zip(ra, rb):
         assert (a is None and b is None) or np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_long_trajectory_every_slot(layout):
+    """40 consecutive steps (t = 1 .. 40, fresh gradients each step) on
+    small ragged weights, D = 2 rank 1, through the one-kernel step: every
+    slot equals the oracle's own 40-step trajectory bit for bit, and so do
+    the row-major outputs of the last step."""
+    w = WL.ragged()
+    w.dims = [(1, 300, 410), (2, 130, 257), (1, 77, 1000)]
+    w.D, w.rank = 2, 1
+    w.steps = list(range(1, 41))
+    _say("40-step trajectory: 3 small ragged weights, D = 2 rank 1, layout", layout)
+    g = GpuWorkload(w, mode="fused_unpack", layout=layout)
+    g.load_state()
+    g.run_steps()
+    slots = list(range(g.q))
+    ora = oracle_slots(w, slots)
+    rep = _check(g.tiles(slots), ora, f"40 steps, {layout}")
+    assert rep["exact"]
+    fp8, sc = g.rowmajor()
+    torch.cuda.synchronize()
+    q, owned, table = oracle.plan(w.dims, w.D, w.rank)
+    o8 = [np.zeros(d, dtype=np.uint8) for d in w.dims]
+    osc = [np.zeros((d[0], -(-d[1] // 128), -(-d[2] // 128)), dtype=np.float32) for d in w.dims]
+    oracle.unpack(w.dims, ora["codes"].reshape(-1), ora["scale_inv"], table, o8, osc)
+    for k in range(owned):
+        p, e, i, j, vr, vc = (int(x) for x in table[k])
+        E, H, W = w.dims[p]
+        got = fp8[p].view(E, H, W)[e, 128 * i:128 * i + vr, 128 * j:128 * j + vc].cpu().numpy()
+        assert np.array_equal(got, o8[p][e, 128 * i:128 * i + vr, 128 * j:128 * j + vc]), k
+        assert float(sc[p].view(osc[p].shape)[e, i, j]) == float(osc[p][e, i, j]), k
