@@ -90,6 +90,36 @@ __device__ __forceinline__ f32x4 load_stream(const f32x4* p) { return __builtin_
 __device__ __forceinline__ void store_stream(f32x4* p, f32x4 v) { __builtin_nontemporal_store(v, p); }
 __device__ __forceinline__ void store_stream(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
 
+// A tile's blocks in the shard arrays (master, m, v, a tile-major gradient:
+// 64 KiB each; codes: 16 KiB) are accessed through buffer instructions,
+// whose cache-policy operand can carry sc1 (device scope) beside nt.  On
+// this part each XCD has its own L2, so a device-scope store is written
+// through the L2 as it is made instead of staying there dirty until
+// evicted; non-temporal loads and nt + sc1 stores measured 1-2.6% faster
+// for every step kernel than non-temporal global loads and stores (the
+// same values land in memory).  The descriptor spans exactly the block: an
+// offset past it would read zero or be dropped, never touch other memory.
+constexpr int kPolicyLoad = 2;        // nt
+constexpr int kPolicyStore = 2 | 16;  // nt sc1
+constexpr uint32_t kRawBufferFlags = 0x00020000u;  // descriptor word 3 of a raw dword buffer
+
+struct TileBlock {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ TileBlock(const void* base, int bytes)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes,
+                                              kRawBufferFlags)) {}
+    __device__ __forceinline__ f32x4 load(int i) const {  // float4 i of the block
+        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, i * 16, 0, kPolicyLoad));
+    }
+    __device__ __forceinline__ void store(int i, const f32x4& v) const {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, i * 16, 0, kPolicyStore);
+    }
+    __device__ __forceinline__ void store_word(int i, uint32_t w) const {  // 32-bit word i
+        __builtin_amdgcn_raw_buffer_store_b32(w, r, i * 4, 0, kPolicyStore);
+    }
+};
+
 __device__ __forceinline__ float abs_max4(float a, const f32x4& x) {
     return fmaxf(fmaxf(a, fmaxf(fabsf(x.x), fabsf(x.y))), fmaxf(fabsf(x.z), fabsf(x.w)));
 }
@@ -140,10 +170,10 @@ constexpr int kStepLdsBytes = 96 * 1024;                 // > half of the 160 Ki
 
 // Gradient of a tile already folded into the tile-major shard.
 struct TileMajorGrad {
-    const f32x4* tile;
+    TileBlock tile;
     typedef f32x4 Raw;
     __device__ __forceinline__ Raw load(int k, const f32x4*) const {
-        return load_stream(tile + k * kStepThreads + threadIdx.x);
+        return tile.load(k * kStepThreads + threadIdx.x);
     }
     __device__ __forceinline__ f32x4 finish(int, const Raw& r) const { return r; }
 };
@@ -297,16 +327,17 @@ __device__ __forceinline__ float step_tile(int64_t tile, float* __restrict__ mas
     f32x4* P = reinterpret_cast<f32x4*>(master) + sbase;
     f32x4* M = reinterpret_cast<f32x4*>(mom1) + sbase;
     f32x4* V = reinterpret_cast<f32x4*>(mom2) + sbase;
+    const TileBlock bP(P, kTileElems * 4), bM(M, kTileElems * 4), bV(V, kTileElems * 4);
 
     f32x4 p[kStepVec], g[kStepVec], m[kStepVec], v[kStepVec];
     typename GradFn::Raw graw[kStepVec];
 #pragma unroll
     for (int k = 0; k < kStepVec; ++k) {
         const int i = k * kStepThreads + threadIdx.x;
-        p[k] = load_stream(P + i);
+        p[k] = bP.load(i);
         graw[k] = grad_at.load(k, P + i);
-        m[k] = load_stream(M + i);
-        v[k] = load_stream(V + i);
+        m[k] = bM.load(i);
+        v[k] = bV.load(i);
     }
 #pragma unroll
     for (int k = 0; k < kStepVec; ++k) g[k] = grad_at.finish(k, graw[k]);
@@ -322,9 +353,9 @@ __device__ __forceinline__ float step_tile(int64_t tile, float* __restrict__ mas
             m[k][l] = ml;
             v[k][l] = vl;
         }
-        store_stream(M + i, m[k]);
-        store_stream(V + i, v[k]);
-        store_stream(P + i, p[k]);
+        bM.store(i, m[k]);
+        bV.store(i, v[k]);
+        bP.store(i, p[k]);
         amax = abs_max4(amax, p[k]);
     }
 #pragma unroll
@@ -347,11 +378,11 @@ __device__ __forceinline__ float step_tile(int64_t tile, float* __restrict__ mas
         if (scale_inv) scale_inv[tile] = scale;
         if (out.scale_cell) *out.scale_cell = scale;
     }
-    uint32_t* C = codes ? codes + base : nullptr;
+    const TileBlock C(codes ? codes + base : nullptr, kTileElems);
 #pragma unroll
     for (int k = 0; k < kStepVec; ++k) {
         const uint32_t word = zero ? 0u : pack_codes(p[k], scale);
-        if (C) store_stream(C + k * kStepThreads + threadIdx.x, word);
+        if (codes) C.store_word(k * kStepThreads + threadIdx.x, word);
         out.put(k, word);
     }
     return scale;
@@ -363,7 +394,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(
     StepScalars s, int64_t n_tiles) {
     extern __shared__ float wave_amax[];
     const int64_t tile = xcd_tile(blockIdx.x, n_tiles);
-    const TileMajorGrad g{reinterpret_cast<const f32x4*>(grad) + tile * (kTileElems / 4)};
+    const TileMajorGrad g{TileBlock(grad + tile * kTileElems, kTileElems * 4)};
     step_tile(tile, master, mom1, mom2, codes, scale_inv, s, g, wave_amax);
 }
 
