@@ -146,8 +146,8 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t n_tiles) {
 // and leaves their final order to the compiler's scheduler, which
 // interleaves part of them with the math (forcing all of them first, or an
 // explicit pipeline one to three float4 ahead, measured 1-8% slower).  The
-// update runs in registers, master/m/v go straight back out, and the new
-// master values stay in VGPRs.  The tile amax: lane shuffles within each
+// update runs in registers, then master/m/v go back out, and the new master
+// values stay in VGPRs.  The tile amax: lane shuffles within each
 // wave, then the 16 wave maxima through LDS (one barrier).  Then the
 // register-held values are quantized and stored as one 32-bit word of 4
 // codes per float4.  HBM sees each input once and each output once.  The
@@ -345,7 +345,6 @@ __device__ __forceinline__ float step_tile(int64_t tile, float* __restrict__ mas
     float amax = 0.0f;
 #pragma unroll
     for (int k = 0; k < kStepVec; ++k) {
-        const int i = k * kStepThreads + threadIdx.x;
 #pragma unroll
         for (int l = 0; l < 4; ++l) {
             float pl = p[k][l], ml = m[k][l], vl = v[k][l];
@@ -354,11 +353,18 @@ __device__ __forceinline__ float step_tile(int64_t tile, float* __restrict__ mas
             m[k][l] = ml;
             v[k][l] = vl;
         }
-        bM.store(i, m[k]);
-        bV.store(i, v[k]);
-        bP.store(i, p[k]);
         amax = abs_max4(amax, p[k]);
     }
+    // master, then m, then v: in the interleaved layout the workgroup writes
+    // its [master | m | v] block front to back (measured 0.6-2.8% faster
+    // than storing each float4's three values as it is done, and than the
+    // order m, v, master)
+#pragma unroll
+    for (int k = 0; k < kStepVec; ++k) bP.store(k * kStepThreads + threadIdx.x, p[k]);
+#pragma unroll
+    for (int k = 0; k < kStepVec; ++k) bM.store(k * kStepThreads + threadIdx.x, m[k]);
+#pragma unroll
+    for (int k = 0; k < kStepVec; ++k) bV.store(k * kStepThreads + threadIdx.x, v[k]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
     if ((threadIdx.x & 63) == 0) wave_amax[threadIdx.x >> 6] = amax;
