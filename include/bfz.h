@@ -75,8 +75,8 @@ typedef struct bfz_plan bfz_plan;
  * three arrays' tiles must not overlap one another.  With m = master +
  * 16384 and v = master + 32768 the state is interleaved: one contiguous
  * 192 KiB block [master | m | v] per tile, so each tile's updated state
- * leaves as a single write stream (on MI355X 4-7% faster than three
- * separate arrays); BFZ_STATE_STRIDE_INTERLEAVED is that stride, 49152.
+ * leaves as a single write stream (on MI355X the one-kernel step is
+ * 2.5% faster than with three separate arrays); BFZ_STATE_STRIDE_INTERLEAVED is that stride, 49152.
  * Larger strides leave gaps between the blocks, which are never read or
  * written.  The gradient, codes and scale_inv keep their tile-major layout
  * whatever this value. */
