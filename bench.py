@@ -262,7 +262,7 @@ def main():
 
     import blockwise_fp8_zero_amd as bfz
     from synth import workloads as WL
-    from tests.gpu_run import GpuWorkload
+    from bench_workload import GpuWorkload
 
     torch.cuda.set_device(0)
     w = WL.BY_NAME[args.workload]()

@@ -1,4 +1,6 @@
-"""Drive one workload through the HIP path (product calls only, no oracle).
+"""Device state of one rank's shard of a synthetic workload, driven through
+the library's calls only (no oracle): used by bench.py, the smoke check and
+the GPU tests.
 
 Inputs are row-major FP32 weights drawn on the device by the seeded
 generator; the path then folds them (pack_shard), steps (adamw_fp8_step)
@@ -14,8 +16,9 @@ from synth import workloads as WL
 TILE_ELEMS = bfz.TILE_ELEMS
 
 
-def hp_for(w, t, pow2=False):
-    return bfz.AdamW(step=t, scale_pow2=int(pow2), **WL.HP)
+def hp_for(t):
+    """The workloads' AdamW hyper-parameters at step counter t."""
+    return bfz.AdamW(step=t, **WL.HP)
 
 
 class GpuWorkload:
@@ -109,23 +112,22 @@ class GpuWorkload:
 
     def step(self, t):
         bfz.adamw_fp8_step(self.master, self.grad, self.m, self.v, self.codes, self.scale_inv,
-                           hp_for(self.w, t, self.pow2))
+                           hp_for(t), scale_pow2=self.pow2)
 
     def fold_step(self, t):
         bfz.fold_adamw_fp8_step(self.plan, self.grad_rm, self.master, self.m, self.v, self.codes,
-                                self.scale_inv, hp_for(self.w, t, self.pow2))
+                                self.scale_inv, hp_for(t), scale_pow2=self.pow2)
 
     def fold_step_unpack(self, t):
         codes, scale = (self.codes, self.scale_inv) if self.tile_codes else (None, None)
         if self.transposed:
             bfz.fold_adamw_fp8_step_unpack_t(self.plan, self.grad_rm, self.master, self.m, self.v,
                                              codes, scale, self.out_fp8, self.out_scale,
-                                             self.out_t, self.out_t_scale,
-                                             hp_for(self.w, t, self.pow2))
+                                             self.out_t, self.out_t_scale, hp_for(t))
             return
         bfz.fold_adamw_fp8_step_unpack(self.plan, self.grad_rm, self.master, self.m, self.v,
-                                       codes, scale, self.out_fp8, self.out_scale,
-                                       hp_for(self.w, t, self.pow2))
+                                       codes, scale, self.out_fp8, self.out_scale, hp_for(t),
+                                       scale_pow2=self.pow2)
 
     def apply(self, t):
         """One step on the current row-major gradients."""

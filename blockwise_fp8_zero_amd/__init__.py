@@ -30,13 +30,15 @@ class BfzError(RuntimeError):
 
 
 class AdamW(C.Structure):
-    """Hyper-parameters of one step; step is the counter t >= 1; scale_pow2
-    selects power-of-two tile scales; state_stride (floats between tiles of
-    master / m / v) is filled in by the step functions from the state
-    tensors' layout -- leave it 0."""
+    """bfz_adamw: the hyper-parameters of one step; step is the counter t >= 1."""
     _fields_ = [("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
-                ("eps", C.c_double), ("weight_decay", C.c_double), ("step", C.c_int64),
-                ("scale_pow2", C.c_int32), ("state_stride", C.c_int64)]
+                ("eps", C.c_double), ("weight_decay", C.c_double), ("step", C.c_int64)]
+
+
+class StepOptions(C.Structure):
+    """bfz_step_options: power-of-two tile scales, and the tile stride of
+    master / m / v (the step functions fill it in from the state tensors)."""
+    _fields_ = [("scale_pow2", C.c_int32), ("reserved", C.c_int32), ("state_stride", C.c_int64)]
 
 
 _lib = None
@@ -63,11 +65,12 @@ def lib():
         L.bfz_paramwise_split.argtypes = [P, i32, i32, P, P]
         L.pack_shard.argtypes = [P, P, P, P]
         L.pack_shard_strided.argtypes = [P, P, P, i64, P]
-        L.adamw_fp8_step.argtypes = [P, P, P, P, P, P, i64, C.POINTER(AdamW), P]
-        L.fold_adamw_fp8_step.argtypes = [P, P, P, P, P, P, P, C.POINTER(AdamW), P]
-        L.fold_adamw_fp8_step_unpack.argtypes = [P, P, P, P, P, P, P, P, P, C.POINTER(AdamW), P]
-        L.fold_adamw_fp8_step_unpack_t.argtypes = [P, P, P, P, P, P, P, P, P, P, P, C.POINTER(AdamW),
-                                                   P]
+        A, O = C.POINTER(AdamW), C.POINTER(StepOptions)
+        L.adamw_fp8_step.argtypes = [P, P, P, P, P, P, i64, A, P]
+        L.adamw_fp8_step_ex.argtypes = [P, P, P, P, P, P, i64, A, O, P]
+        L.fold_adamw_fp8_step.argtypes = [P, P, P, P, P, P, P, A, O, P]
+        L.fold_adamw_fp8_step_unpack.argtypes = [P, P, P, P, P, P, P, P, P, A, O, P]
+        L.fold_adamw_fp8_step_unpack_t.argtypes = [P, P, P, P, P, P, P, P, P, P, P, A, O, P]
         L.unpack_fp8.argtypes = [P, P, P, P, P, P]
         L.bfz_e4m3_encode.argtypes = [P, P, i64, P]
         L.bfz_transpose_pow2.argtypes = [P, P, P, P, P, P]
@@ -118,11 +121,13 @@ def _tile_array(t, q, name):
     raise TypeError(f"{name}: need a contiguous tensor or a (tiles, 16384) view of unit inner stride")
 
 
-def _state(master, m, v, q, hp):
-    """Pointers of master, m, v and a copy of hp whose state_stride is their
+def _hparams(hp):
+    return AdamW(**hp) if isinstance(hp, dict) else hp
+
+
+def _state(master, m, v, q, scale_pow2):
+    """Pointers of master, m, v and the step options: scale_pow2 and their
     common tile stride (they must agree; irrelevant when q <= 1)."""
-    if isinstance(hp, dict):
-        hp = AdamW(**hp)
     arrs = [_tile_array(t, q, n) for t, n in ((master, "master"), (m, "m"), (v, "v"))]
     strides = {st for _, st in arrs if st is not None}
     if q <= 1 or not strides:
@@ -131,33 +136,30 @@ def _state(master, m, v, q, hp):
         stride = strides.pop()
     else:
         raise ValueError(f"master, m and v have different tile strides {sorted(strides)}")
-    if hp.state_stride not in (0, stride):
-        raise ValueError(f"hp.state_stride {hp.state_stride} disagrees with the tensors' tile "
-                         f"stride {stride}")
-    hp = AdamW.from_buffer_copy(hp)
-    hp.state_stride = 0 if stride == TILE_ELEMS else stride
-    return [a for a, _ in arrs], hp
+    opts = StepOptions(scale_pow2=int(bool(scale_pow2)), reserved=0,
+                       state_stride=0 if stride == TILE_ELEMS else stride)
+    return [a for a, _ in arrs], opts
 
 
 class Plan:
     """Rank `rank`'s block-wise split of the weights `dims` over D ranks.
 
     dims: sequence of (E, H, W) (E experts of H x W; E = 1 for a matrix).
-    upload=True copies the tile table to the current device (needed before
-    pack_shard / unpack_fp8); the planner itself runs on the host.
+    The planner runs on the host; bfz_plan_create copies the tile table to
+    the current device when a device is visible (on a host without one the
+    plan is host-only: table queries work, device calls raise).
     """
 
-    def __init__(self, dims, D=1, rank=0, upload=True):
+    def __init__(self, dims, D=1, rank=0):
         self.dims = [tuple(int(x) for x in d) for d in dims]
         arr = (C.c_int64 * (3 * max(1, len(self.dims))))(*[x for d in self.dims for x in d])
         h = C.c_void_p()
         _check(lib().bfz_plan_create(C.cast(arr, C.c_void_p), len(self.dims), D, rank, C.byref(h)))
         self._h = h
         self.D, self.rank = D, rank
-        if upload:
-            self.upload()
 
     def upload(self):
+        """Copy the table to the current device if the plan has none yet."""
         _check(lib().bfz_plan_upload(self._h))
 
     @property
@@ -212,13 +214,34 @@ def paramwise_split(dims, D):
     return bop, be
 
 
-def _ptr_array(tensors, dtype, name, n):
+def _ptr_array(tensors, dtype, name, sizes):
+    """Host array of the per-weight device pointers; tensor p (or None) must
+    hold at least sizes[p] elements -- the kernels address it through the
+    plan's table, so a smaller tensor would be read or written past its end."""
+    n = len(sizes)
+    if len(tensors) > n:
+        raise ValueError(f"{name}: {len(tensors)} tensors for {n} weights")
     arr = (C.c_void_p * max(1, n))()
     for k in range(n):
         t = tensors[k] if k < len(tensors) else None
         if t is not None:
-            arr[k] = _dev(t, dtype, f"{name}[{k}]").value
+            arr[k] = _dev(t, dtype, f"{name}[{k}]", sizes[k]).value
     return arr
+
+
+def _weight_sizes(plan):
+    """Elements of each row-major weight (E H W)."""
+    return [E * H * W for E, H, W in plan.dims]
+
+
+def _grid_sizes(plan):
+    """Cells of each row-major scale grid (E ceil(H/128) ceil(W/128))."""
+    return [E * (-(-H // TILE)) * (-(-W // TILE)) for E, H, W in plan.dims]
+
+
+def _t_grid_sizes(plan):
+    """Cells of each transposed copy's scale grid (E W ceil(H/128))."""
+    return [E * W * (-(-H // TILE)) for E, H, W in plan.dims]
 
 
 def pack_shard(plan: Plan, srcs, dst, stream=None):
@@ -228,7 +251,7 @@ def pack_shard(plan: Plan, srcs, dst, stream=None):
     S floats apart, e.g. master = state[:, 0] of the interleaved layout
     (pack_shard_strided)."""
     import torch
-    arr = _ptr_array(srcs, torch.float32, "srcs", len(plan.dims))
+    arr = _ptr_array(srcs, torch.float32, "srcs", _weight_sizes(plan))
     d, stride = _tile_array(dst, plan.shard_tiles, "dst")
     if stride in (None, TILE_ELEMS):
         _check(lib().pack_shard(plan.handle, C.cast(arr, C.c_void_p), d, _stream(stream)))
@@ -244,18 +267,20 @@ def pack_shard_strided(plan: Plan, srcs, dst, dst_stride, stream=None):
     import torch
     q = plan.shard_tiles
     need = (q - 1) * int(dst_stride) + TILE_ELEMS if q else 0
-    arr = _ptr_array(srcs, torch.float32, "srcs", len(plan.dims))
+    arr = _ptr_array(srcs, torch.float32, "srcs", _weight_sizes(plan))
     d = _dev(dst, torch.float32, "dst", need)
     _check(lib().pack_shard_strided(plan.handle, C.cast(arr, C.c_void_p), d, int(dst_stride),
                                     _stream(stream)))
 
 
-def adamw_fp8_step(master, grad, m, v, codes, scale_inv, hp, n_tiles=None, stream=None):
+def adamw_fp8_step(master, grad, m, v, codes, scale_inv, hp, n_tiles=None, scale_pow2=False,
+                   stream=None):
     """Fused AdamW + per-tile E4M3 requant over n_tiles whole tiles (default:
     all of master).  hp: AdamW, or a dict of its fields.  master / m / v:
     contiguous, or (tiles, 16384) views with a common tile stride (the
     interleaved layout: state[:, 0], state[:, 1], state[:, 2] of a
-    (q, 3, 16384) tensor)."""
+    (q, 3, 16384) tensor).  Plain scales on three tile-major arrays call
+    adamw_fp8_step itself; anything else adamw_fp8_step_ex."""
     import torch
     if n_tiles is None:
         if master.dim() == 2 and master.shape[1] == TILE_ELEMS:
@@ -265,77 +290,80 @@ def adamw_fp8_step(master, grad, m, v, codes, scale_inv, hp, n_tiles=None, strea
         else:
             n_tiles = master.numel() // TILE_ELEMS
     n = n_tiles * TILE_ELEMS
-    (p, mm, vv), hp = _state(master, m, v, n_tiles, hp)
+    (p, mm, vv), opts = _state(master, m, v, n_tiles, scale_pow2)
     args = [p, _dev(grad, torch.float32, "grad", n), mm, vv,
             _dev(codes, torch.uint8, "codes", n), _dev(scale_inv, torch.float32, "scale_inv", n_tiles)]
-    _check(lib().adamw_fp8_step(*args, n_tiles, C.byref(hp), _stream(stream)))
+    hp = _hparams(hp)
+    if opts.scale_pow2 == 0 and opts.state_stride == 0:
+        _check(lib().adamw_fp8_step(*args, n_tiles, C.byref(hp), _stream(stream)))
+    else:
+        _check(lib().adamw_fp8_step_ex(*args, n_tiles, C.byref(hp), C.byref(opts), _stream(stream)))
 
 
-def fold_adamw_fp8_step(plan: Plan, grads, master, m, v, codes, scale_inv, hp, stream=None):
+def fold_adamw_fp8_step(plan: Plan, grads, master, m, v, codes, scale_inv, hp, scale_pow2=False,
+                        stream=None):
     """pack_shard of the row-major gradients grads[p] and adamw_fp8_step over
     the whole shard in one pass (the folded gradient is never stored)."""
     import torch
-    arr = _ptr_array(grads, torch.float32, "grads", len(plan.dims))
+    arr = _ptr_array(grads, torch.float32, "grads", _weight_sizes(plan))
     q = plan.shard_tiles
     n = q * TILE_ELEMS
-    (p, mm, vv), hp = _state(master, m, v, q, hp)
+    (p, mm, vv), opts = _state(master, m, v, q, scale_pow2)
     args = [p, mm, vv, _dev(codes, torch.uint8, "codes", n),
             _dev(scale_inv, torch.float32, "scale_inv", q)]
-    _check(lib().fold_adamw_fp8_step(plan.handle, C.cast(arr, C.c_void_p), *args, C.byref(hp),
-                                     _stream(stream)))
+    _check(lib().fold_adamw_fp8_step(plan.handle, C.cast(arr, C.c_void_p), *args,
+                                     C.byref(_hparams(hp)), C.byref(opts), _stream(stream)))
 
 
 def fold_adamw_fp8_step_unpack(plan: Plan, grads, master, m, v, codes, scale_inv, dst_fp8,
-                               dst_scale, hp, stream=None):
+                               dst_scale, hp, scale_pow2=False, stream=None):
     """fold_adamw_fp8_step and unpack_fp8 in one pass.  codes / scale_inv may
     both be None (no tile-major copy of the codes)."""
     import torch
     if (codes is None) != (scale_inv is None):
         raise ValueError("codes and scale_inv: give both or neither")
-    n = len(plan.dims)
     q = plan.shard_tiles
-    g = _ptr_array(grads, torch.float32, "grads", n)
-    a8 = _ptr_array(dst_fp8, torch.uint8, "dst_fp8", n)
-    asc = _ptr_array(dst_scale, torch.float32, "dst_scale", n)
+    g = _ptr_array(grads, torch.float32, "grads", _weight_sizes(plan))
+    a8 = _ptr_array(dst_fp8, torch.uint8, "dst_fp8", _weight_sizes(plan))
+    asc = _ptr_array(dst_scale, torch.float32, "dst_scale", _grid_sizes(plan))
     c = None if codes is None else _dev(codes, torch.uint8, "codes", q * TILE_ELEMS)
     sc = None if scale_inv is None else _dev(scale_inv, torch.float32, "scale_inv", q)
-    (p, mm, vv), hp = _state(master, m, v, q, hp)
+    (p, mm, vv), opts = _state(master, m, v, q, scale_pow2)
     _check(lib().fold_adamw_fp8_step_unpack(
-        plan.handle, C.cast(g, C.c_void_p), p, mm, vv,
-        c, sc, C.cast(a8, C.c_void_p), C.cast(asc, C.c_void_p), C.byref(hp), _stream(stream)))
+        plan.handle, C.cast(g, C.c_void_p), p, mm, vv, c, sc, C.cast(a8, C.c_void_p),
+        C.cast(asc, C.c_void_p), C.byref(_hparams(hp)), C.byref(opts), _stream(stream)))
 
 
 def fold_adamw_fp8_step_unpack_t(plan: Plan, grads, master, m, v, codes, scale_inv, dst_fp8,
                                  dst_scale, dst_t, dst_t_scale, hp, stream=None):
     """fold_adamw_fp8_step_unpack with power-of-two scales plus the transposed
     copy (dst_t[p] uint8 (E, W, H), dst_t_scale[p] float32 (E, W, ceil(H/128)))
-    in one pass.  hp must have scale_pow2 set; codes / scale_inv may both be None."""
+    in one pass (power-of-two scales are implied); codes / scale_inv may
+    both be None."""
     import torch
     if (codes is None) != (scale_inv is None):
         raise ValueError("codes and scale_inv: give both or neither")
-    n = len(plan.dims)
     q = plan.shard_tiles
-    g = _ptr_array(grads, torch.float32, "grads", n)
-    a8 = _ptr_array(dst_fp8, torch.uint8, "dst_fp8", n)
-    asc = _ptr_array(dst_scale, torch.float32, "dst_scale", n)
-    t8 = _ptr_array(dst_t, torch.uint8, "dst_t", n)
-    tsc = _ptr_array(dst_t_scale, torch.float32, "dst_t_scale", n)
+    g = _ptr_array(grads, torch.float32, "grads", _weight_sizes(plan))
+    a8 = _ptr_array(dst_fp8, torch.uint8, "dst_fp8", _weight_sizes(plan))
+    asc = _ptr_array(dst_scale, torch.float32, "dst_scale", _grid_sizes(plan))
+    t8 = _ptr_array(dst_t, torch.uint8, "dst_t", _weight_sizes(plan))
+    tsc = _ptr_array(dst_t_scale, torch.float32, "dst_t_scale", _t_grid_sizes(plan))
     c = None if codes is None else _dev(codes, torch.uint8, "codes", q * TILE_ELEMS)
     sc = None if scale_inv is None else _dev(scale_inv, torch.float32, "scale_inv", q)
-    (p, mm, vv), hp = _state(master, m, v, q, hp)
+    (p, mm, vv), opts = _state(master, m, v, q, True)
     _check(lib().fold_adamw_fp8_step_unpack_t(
-        plan.handle, C.cast(g, C.c_void_p), p, mm, vv,
-        c, sc, C.cast(a8, C.c_void_p), C.cast(asc, C.c_void_p), C.cast(t8, C.c_void_p),
-        C.cast(tsc, C.c_void_p), C.byref(hp), _stream(stream)))
+        plan.handle, C.cast(g, C.c_void_p), p, mm, vv, c, sc, C.cast(a8, C.c_void_p),
+        C.cast(asc, C.c_void_p), C.cast(t8, C.c_void_p), C.cast(tsc, C.c_void_p),
+        C.byref(_hparams(hp)), C.byref(opts), _stream(stream)))
 
 
 def unpack_fp8(plan: Plan, codes, scale_inv, dst_fp8, dst_scale, stream=None):
     """Unfold the shard's codes and scales into row-major uint8 weights
     dst_fp8[p] (E, H, W) and scale grids dst_scale[p] (E, ceil(H/128), ceil(W/128))."""
     import torch
-    n = len(plan.dims)
-    a8 = _ptr_array(dst_fp8, torch.uint8, "dst_fp8", n)
-    asc = _ptr_array(dst_scale, torch.float32, "dst_scale", n)
+    a8 = _ptr_array(dst_fp8, torch.uint8, "dst_fp8", _weight_sizes(plan))
+    asc = _ptr_array(dst_scale, torch.float32, "dst_scale", _grid_sizes(plan))
     q = plan.shard_tiles
     _check(lib().unpack_fp8(plan.handle, _dev(codes, torch.uint8, "codes", q * TILE_ELEMS),
                             _dev(scale_inv, torch.float32, "scale_inv", q),
@@ -346,10 +374,9 @@ def transpose_pow2(plan: Plan, codes, scale_inv, dst_t, dst_t_scale, stream=None
     """Transposed copy of the shard's power-of-two-quantized tiles by exponent
     edits: dst_t[p] uint8 (E, W, H), dst_t_scale[p] float32 (E, W, ceil(H/128))."""
     import torch
-    n = len(plan.dims)
     q = plan.shard_tiles
-    a8 = _ptr_array(dst_t, torch.uint8, "dst_t", n)
-    asc = _ptr_array(dst_t_scale, torch.float32, "dst_t_scale", n)
+    a8 = _ptr_array(dst_t, torch.uint8, "dst_t", _weight_sizes(plan))
+    asc = _ptr_array(dst_t_scale, torch.float32, "dst_t_scale", _t_grid_sizes(plan))
     _check(lib().bfz_transpose_pow2(plan.handle, _dev(codes, torch.uint8, "codes", q * TILE_ELEMS),
                                     _dev(scale_inv, torch.float32, "scale_inv", q),
                                     C.cast(a8, C.c_void_p), C.cast(asc, C.c_void_p),

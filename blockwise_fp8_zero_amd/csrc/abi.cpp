@@ -26,7 +26,9 @@ constexpr int64_t kMaxLaunchTiles = (int64_t(1) << 32) / 1024 - 1;
 // The plan's tile table lives on the device it was uploaded to: a call made
 // with another device current would hand that device a foreign pointer.
 int check_plan(const bfz_plan* plan, const char* where) {
-    if (!plan->d_entries) return fail(BFZ_ESTATE, "%s: plan not uploaded (bfz_plan_upload)", where);
+    if (!plan->d_entries)
+        return fail(BFZ_ESTATE, "%s: plan has no device table (no HIP device was visible when it "
+                    "was created; see bfz_plan_upload)", where);
     for (const Segment& seg : plan->segments)
         if (seg.n_slots > kMaxLaunchTiles)
             return fail(BFZ_EINVAL, "%s: %lld slots in one launch segment, more than %lld", where,
@@ -146,16 +148,22 @@ namespace {
 // The step's scalars, formed in double and rounded to binary32 once each:
 // the bias corrections 1 - beta^t enter as lr / (1 - beta1^t) and
 // sqrt(1 - beta2^t), as in the Int8AdamW step (lpnh.cn essay, section 4.3).
-int make_scalars(const bfz_adamw* hp, StepScalars* s, const char* where) {
-    s->state_stride = hp->state_stride == 0 ? kTileElems : hp->state_stride;
+// opts may be NULL (every option 0).  eps must be positive: it keeps the
+// denominator of an all-zero slot (every padding slot) away from 0 / 0.
+int make_scalars(const bfz_adamw* hp, const bfz_step_options* opts, StepScalars* s,
+                 const char* where) {
+    const bfz_step_options none{};
+    if (!opts) opts = &none;
+    if (opts->reserved != 0) return fail(BFZ_EINVAL, "%s: bfz_step_options.reserved must be 0", where);
+    s->state_stride = opts->state_stride == 0 ? kTileElems : opts->state_stride;
     if (!valid_stride(s->state_stride))
         return fail(BFZ_EINVAL, "%s: state_stride %lld is not 0 or a multiple of 4 in [16384, 2^26]",
-                    where, (long long)hp->state_stride);
+                    where, (long long)opts->state_stride);
     const double lr = hp->lr, b1 = hp->beta1, b2 = hp->beta2, eps = hp->eps, wd = hp->weight_decay;
-    if (!std::isfinite(lr) || !std::isfinite(eps) || !std::isfinite(wd) || !(eps >= 0.0) ||
+    if (!std::isfinite(lr) || !std::isfinite(eps) || !std::isfinite(wd) || !(eps > 0.0) ||
         !(b1 >= 0.0 && b1 < 1.0) || !(b2 >= 0.0 && b2 < 1.0) || hp->step < 1)
         return fail(BFZ_EINVAL,
-                    "%s: need finite lr/eps/weight_decay, eps >= 0, 0 <= beta < 1, step >= 1", where);
+                    "%s: need finite lr/eps/weight_decay, eps > 0, 0 <= beta < 1, step >= 1", where);
     const double t = double(hp->step);
     s->b1 = float(b1);
     s->c1 = float(1.0 - b1);
@@ -166,7 +174,7 @@ int make_scalars(const bfz_adamw* hp, StepScalars* s, const char* where) {
     s->eps = float(eps);
     s->decay = float(lr * wd);
     s->has_decay = wd != 0.0;
-    s->pow2 = hp->scale_pow2 != 0;
+    s->pow2 = opts->scale_pow2 != 0;
     return BFZ_OK;
 }
 
@@ -178,31 +186,47 @@ int check_state(float* master, float* m, float* v, uint8_t* codes, float* scale_
     return BFZ_OK;
 }
 
+int step_tiles(float* master, const float* grad, float* m, float* v, uint8_t* codes,
+               float* scale_inv, int64_t n_tiles, const bfz_adamw* hp,
+               const bfz_step_options* opts, void* stream, const char* where) {
+    if (!master || !grad || !m || !v || !codes || !scale_inv || !hp)
+        return fail(BFZ_EINVAL, "%s: null pointer", where);
+    if (n_tiles < 0 || n_tiles > kMaxLaunchTiles)
+        return fail(BFZ_EINVAL, "%s: n_tiles %lld outside [0, %lld]", where, (long long)n_tiles,
+                    (long long)kMaxLaunchTiles);
+    if (!aligned(grad, 16))
+        return fail(BFZ_EALIGN, "%s: master, grad, m, v and codes must be 16-byte aligned", where);
+    int rc = check_state(master, m, v, codes, scale_inv, where);
+    if (rc) return rc;
+    StepScalars s;
+    rc = make_scalars(hp, opts, &s, where);
+    if (rc) return rc;
+    int err = launch_step(master, grad, m, v, codes, scale_inv, n_tiles, s, stream);
+    if (err != hipSuccess) return hip_fail(where, err);
+    return BFZ_OK;
+}
+
 }  // namespace
 
 extern "C" int adamw_fp8_step(float* master, const float* grad, float* m, float* v,
                               uint8_t* codes, float* scale_inv, int64_t n_tiles,
                               const bfz_adamw* hp, void* stream) {
-    if (!master || !grad || !m || !v || !codes || !scale_inv || !hp)
-        return fail(BFZ_EINVAL, "adamw_fp8_step: null pointer");
-    if (n_tiles < 0 || n_tiles > kMaxLaunchTiles)
-        return fail(BFZ_EINVAL, "adamw_fp8_step: n_tiles %lld outside [0, %lld]", (long long)n_tiles,
-                    (long long)kMaxLaunchTiles);
-    if (!aligned(grad, 16))
-        return fail(BFZ_EALIGN, "adamw_fp8_step: master, grad, m, v and codes must be 16-byte aligned");
-    int rc = check_state(master, m, v, codes, scale_inv, "adamw_fp8_step");
-    if (rc) return rc;
-    StepScalars s;
-    rc = make_scalars(hp, &s, "adamw_fp8_step");
-    if (rc) return rc;
-    int err = launch_step(master, grad, m, v, codes, scale_inv, n_tiles, s, stream);
-    if (err != hipSuccess) return hip_fail("adamw_fp8_step", err);
-    return BFZ_OK;
+    return step_tiles(master, grad, m, v, codes, scale_inv, n_tiles, hp, nullptr, stream,
+                      "adamw_fp8_step");
+}
+
+extern "C" int adamw_fp8_step_ex(float* master, const float* grad, float* m, float* v,
+                                 uint8_t* codes, float* scale_inv, int64_t n_tiles,
+                                 const bfz_adamw* hp, const bfz_step_options* opts,
+                                 void* stream) {
+    return step_tiles(master, grad, m, v, codes, scale_inv, n_tiles, hp, opts, stream,
+                      "adamw_fp8_step_ex");
 }
 
 extern "C" int fold_adamw_fp8_step(const bfz_plan* plan, const float* const* grad, float* master,
                                    float* m, float* v, uint8_t* codes, float* scale_inv,
-                                   const bfz_adamw* hp, void* stream) {
+                                   const bfz_adamw* hp, const bfz_step_options* opts,
+                                   void* stream) {
     if (!plan || !grad || !master || !m || !v || !codes || !scale_inv || !hp)
         return fail(BFZ_EINVAL, "fold_adamw_fp8_step: null pointer");
     int rc = check_plan(plan, "fold_adamw_fp8_step");
@@ -215,7 +239,7 @@ extern "C" int fold_adamw_fp8_step(const bfz_plan* plan, const float* const* gra
     rc = check_state(master, m, v, codes, scale_inv, "fold_adamw_fp8_step");
     if (rc) return rc;
     StepScalars s;
-    rc = make_scalars(hp, &s, "fold_adamw_fp8_step");
+    rc = make_scalars(hp, opts, &s, "fold_adamw_fp8_step");
     if (rc) return rc;
     for (const Segment& seg : plan->segments) {
         PackArgs args{};
@@ -232,7 +256,7 @@ extern "C" int fold_adamw_fp8_step_unpack(const bfz_plan* plan, const float* con
                                           float* master, float* m, float* v, uint8_t* codes,
                                           float* scale_inv, uint8_t* const* dst_fp8,
                                           float* const* dst_scale, const bfz_adamw* hp,
-                                          void* stream) {
+                                          const bfz_step_options* opts, void* stream) {
     const char* where = "fold_adamw_fp8_step_unpack";
     if (!plan || !grad || !master || !m || !v || !dst_fp8 || !dst_scale || !hp)
         return fail(BFZ_EINVAL, "%s: null pointer", where);
@@ -255,7 +279,7 @@ extern "C" int fold_adamw_fp8_step_unpack(const bfz_plan* plan, const float* con
     if (scale_inv && !aligned(scale_inv, 4))
         return fail(BFZ_EALIGN, "%s: scale_inv must be 4-byte aligned", where);
     StepScalars s;
-    rc = make_scalars(hp, &s, where);
+    rc = make_scalars(hp, opts, &s, where);
     if (rc) return rc;
     for (const Segment& seg : plan->segments) {
         PackArgs in{};
@@ -280,16 +304,16 @@ extern "C" int fold_adamw_fp8_step_unpack_t(const bfz_plan* plan, const float* c
                                             float* scale_inv, uint8_t* const* dst_fp8,
                                             float* const* dst_scale, uint8_t* const* dst_t,
                                             float* const* dst_t_scale, const bfz_adamw* hp,
-                                            void* stream) {
+                                            const bfz_step_options* opts, void* stream) {
     const char* where = "fold_adamw_fp8_step_unpack_t";
     if (!plan || !grad || !master || !m || !v || !dst_fp8 || !dst_scale || !dst_t || !dst_t_scale ||
         !hp)
         return fail(BFZ_EINVAL, "%s: null pointer", where);
     if (!codes != !scale_inv)
         return fail(BFZ_EINVAL, "%s: codes and scale_inv must be both given or both NULL", where);
-    if (!hp->scale_pow2)
-        return fail(BFZ_EINVAL, "%s: the transposed copy needs power-of-two scales (scale_pow2)",
-                    where);
+    if (!opts || !opts->scale_pow2)
+        return fail(BFZ_EINVAL, "%s: the transposed copy needs power-of-two scales "
+                    "(bfz_step_options.scale_pow2)", where);
     int rc = check_plan(plan, where);
     if (rc) return rc;
     rc = check_weights(plan, reinterpret_cast<const void* const*>(grad), where);
@@ -311,7 +335,7 @@ extern "C" int fold_adamw_fp8_step_unpack_t(const bfz_plan* plan, const float* c
     if (scale_inv && !aligned(scale_inv, 4))
         return fail(BFZ_EALIGN, "%s: scale_inv must be 4-byte aligned", where);
     StepScalars s;
-    rc = make_scalars(hp, &s, where);
+    rc = make_scalars(hp, opts, &s, where);
     if (rc) return rc;
     for (const Segment& seg : plan->segments) {
         PackArgs in{};

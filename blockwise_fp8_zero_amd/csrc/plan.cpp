@@ -29,6 +29,26 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int build_plan(const int64_t* dims, int32_t n_weights, int32_t D, int32_t rank, int64_t total,
                bfz_plan** out);
 
+// Copies the table to the current device (the plan has no device copy yet).
+int upload_table(bfz_plan* plan, int dev, const char* where) {
+    using namespace bfz;
+    size_t bytes = std::max<size_t>(1, plan->entries.size()) * sizeof(TileEntry);
+    TileEntry* d = nullptr;
+    hipError_t err = hipMalloc(reinterpret_cast<void**>(&d), bytes);
+    if (err != hipSuccess) return fail(BFZ_EHIP, "%s: hipMalloc: %s", where, hipGetErrorString(err));
+    if (!plan->entries.empty()) {
+        err = hipMemcpy(d, plan->entries.data(), plan->entries.size() * sizeof(TileEntry),
+                        hipMemcpyHostToDevice);
+        if (err != hipSuccess) {
+            (void)hipFree(d);
+            return fail(BFZ_EHIP, "%s: hipMemcpy: %s", where, hipGetErrorString(err));
+        }
+    }
+    plan->d_entries = d;
+    plan->device = dev;
+    return BFZ_OK;
+}
+
 }  // namespace
 
 extern "C" int bfz_plan_create(const int64_t* dims, int32_t n_weights, int32_t D, int32_t rank,
@@ -58,11 +78,26 @@ extern "C" int bfz_plan_create(const int64_t* dims, int32_t n_weights, int32_t D
     if (ceil_div(total, D) > int64_t(INT32_MAX))
         return fail(BFZ_EINVAL, "bfz_plan_create: %lld tiles over %d ranks is more than 2^31 - 1 per rank",
                     (long long)total, D);
+    int rc;
     try {
-        return build_plan(dims, n_weights, D, rank, total, out);
+        rc = build_plan(dims, n_weights, D, rank, total, out);
     } catch (const std::bad_alloc&) {
         return fail(BFZ_EINVAL, "bfz_plan_create: out of host memory");
     }
+    if (rc) return rc;
+    // The device copy goes to the current device when the process sees one;
+    // without a device the plan stays host-only (queries work, device calls
+    // report BFZ_ESTATE).
+    int count = 0, dev = -1;
+    if (hipGetDeviceCount(&count) == hipSuccess && count > 0 && hipGetDevice(&dev) == hipSuccess) {
+        rc = upload_table(*out, dev, "bfz_plan_create");
+        if (rc) {
+            delete *out;
+            *out = nullptr;
+            return rc;
+        }
+    }
+    return BFZ_OK;
 }
 
 namespace {
@@ -200,21 +235,7 @@ extern "C" int bfz_plan_upload(bfz_plan* plan) {
         if (plan->device == dev) return BFZ_OK;
         return fail(BFZ_EINVAL, "bfz_plan_upload: plan already on device %d", plan->device);
     }
-    size_t bytes = std::max<size_t>(1, plan->entries.size()) * sizeof(TileEntry);
-    TileEntry* d = nullptr;
-    err = hipMalloc(reinterpret_cast<void**>(&d), bytes);
-    if (err != hipSuccess) return fail(BFZ_EHIP, "bfz_plan_upload: hipMalloc: %s", hipGetErrorString(err));
-    if (!plan->entries.empty()) {
-        err = hipMemcpy(d, plan->entries.data(), plan->entries.size() * sizeof(TileEntry),
-                        hipMemcpyHostToDevice);
-        if (err != hipSuccess) {
-            (void)hipFree(d);
-            return fail(BFZ_EHIP, "bfz_plan_upload: hipMemcpy: %s", hipGetErrorString(err));
-        }
-    }
-    plan->d_entries = d;
-    plan->device = dev;
-    return BFZ_OK;
+    return upload_table(plan, dev, "bfz_plan_upload");
 }
 
 extern "C" int64_t bfz_plan_shard_tiles(const bfz_plan* plan) { return plan ? plan->quota : -1; }

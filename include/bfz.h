@@ -23,11 +23,11 @@
  *   - A tile is 16384 contiguous elements: 128 rows of 128, row-major.
  *     A shard is q tiles back to back (q = bfz_plan_shard_tiles), except
  *     the FP32 optimizer state (master, m, v), whose tiles may sit a stride
- *     apart (bfz_adamw.state_stride; e.g. one [master | m | v] block per
- *     tile) -- same values, same order, other addresses.
+ *     apart (bfz_step_options.state_stride; e.g. one [master | m | v] block
+ *     per tile) -- same values, same order, other addresses.
  *   - Device pointers are caller-owned (the library never frees them); the
  *     library allocates only the plan's small device table, in
- *     bfz_plan_upload, freed by bfz_plan_destroy.
+ *     bfz_plan_create (or bfz_plan_upload), freed by bfz_plan_destroy.
  *   - pack_shard(_strided), adamw_fp8_step, fold_adamw_fp8_step,
  *     fold_adamw_fp8_step_unpack and unpack_fp8 are asynchronous on the HIP
  *     stream passed as `stream` (NULL = the null stream): they only enqueue
@@ -48,22 +48,31 @@ extern "C" {
 #define BFZ_TILE_DIM 128
 #define BFZ_TILE_ELEMS 16384
 /* The interleaved state layout's tile stride, in floats (see
- * bfz_adamw.state_stride): one [master | m | v] block per tile. */
+ * bfz_step_options.state_stride): one [master | m | v] block per tile. */
 #define BFZ_STATE_STRIDE_INTERLEAVED 49152
 
 #define BFZ_OK 0
 #define BFZ_EINVAL (-1) /* null pointer, bad size or shape, bad hyper-parameter */
 #define BFZ_EALIGN (-2) /* a pointer lacks its required alignment */
 #define BFZ_EHIP (-3)   /* a HIP runtime call or kernel launch failed */
-#define BFZ_ESTATE (-4) /* plan not uploaded, or uploaded to another device than the current one */
+#define BFZ_ESTATE (-4) /* plan has no device table, or its table is on another device than the current one */
 
 /* The block-wise split of one rank: the lookup table of its tiles. */
 typedef struct bfz_plan bfz_plan;
 
-/* AdamW hyper-parameters and the options of one step.  step is the
- * counter t >= 1 of the step being taken (the first step is t = 1).
- * Requires lr, eps, weight_decay finite, eps >= 0, 0 <= beta1 < 1,
- * 0 <= beta2 < 1.
+/* AdamW hyper-parameters of one step (the update of section 4.3 of the
+ * lpnh.cn optimizer-state quantization essay).  step is the counter t >= 1
+ * of the step being taken (the first step is t = 1).  Requires lr and
+ * weight_decay finite, eps finite and > 0 (eps is the denominator's floor:
+ * with eps = 0 an all-zero slot would compute 0 / 0), 0 <= beta1 < 1,
+ * 0 <= beta2 < 1.  48 bytes; every step call reads exactly this struct. */
+typedef struct {
+    double lr, beta1, beta2, eps, weight_decay;
+    int64_t step;
+} bfz_adamw;
+
+/* Options of a step beyond the hyper-parameters, taken by the _ex and fold
+ * entry points (a NULL pointer means every field 0, the defaults).
  * scale_pow2 = 0: scale_inv = amax / 448.  scale_pow2 != 0: scale_inv is
  * the smallest power of two 2^T with 448 * 2^T >= amax (T >= -149), so
  * every quotient p / scale_inv is exact and codes can later be moved
@@ -76,16 +85,16 @@ typedef struct bfz_plan bfz_plan;
  * 16384 and v = master + 32768 the state is interleaved: one contiguous
  * 192 KiB block [master | m | v] per tile, so each tile's updated state
  * leaves as a single write stream (on MI355X the one-kernel step is
- * 2.5% faster than with three separate arrays); BFZ_STATE_STRIDE_INTERLEAVED is that stride, 49152.
- * Larger strides leave gaps between the blocks, which are never read or
- * written.  The gradient, codes and scale_inv keep their tile-major layout
- * whatever this value. */
+ * 2.5% faster than with three separate arrays); BFZ_STATE_STRIDE_INTERLEAVED
+ * is that stride, 49152.  Larger strides leave gaps between the blocks,
+ * which are never read or written.  The gradient, codes and scale_inv keep
+ * their tile-major layout whatever this value.
+ * reserved must be 0 (BFZ_EINVAL otherwise). */
 typedef struct {
-    double lr, beta1, beta2, eps, weight_decay;
-    int64_t step;
     int32_t scale_pow2;
+    int32_t reserved;
     int64_t state_stride;
-} bfz_adamw;
+} bfz_step_options;
 
 /*
  * Build rank `rank`'s block-wise split of n_params weights.
@@ -99,21 +108,27 @@ typedef struct {
  * [r q, min((r + 1) q, T)); a shorter shard ends in all-zero padding slots
  * so that every shard is q tiles (section "Block-wise split" pads buckets to
  * the largest one; the contiguous equal quota is this library's reading of
- * how the page deals tiles to ranks).  Host only: touches no GPU.
+ * how the page deals tiles to ranks).
+ * The table is built on the host and, when the process sees a HIP device,
+ * copied to the current device (about 24 bytes per tile, allocated here and
+ * freed by bfz_plan_destroy; synchronous).  Every call that takes the plan
+ * then needs that device to be current.  On a host with no HIP device the
+ * plan is host-only: the queries below work, the device calls return
+ * BFZ_ESTATE.
  * On success *out receives a new plan.  Errors: BFZ_EINVAL for null
  * pointers, n_params < 1, D < 1, rank outside [0, D), a dimension < 1,
  * H, W > 2^31 - 1, a weight of more than 2^31 - 1 tiles, a quota q of more
  * than 2^31 - 1 tiles, or too little host memory for the table (76 bytes
- * per slot).
+ * per slot); BFZ_EHIP if the device copy fails.
  */
 int bfz_plan_create(const int64_t* dims, int32_t n_params, int32_t D, int32_t rank,
                     bfz_plan** out);
 
-/* Copy the plan's tile table to the current HIP device (allocates about
- * 24 bytes per tile; synchronous).  Needed once before any call that takes
- * the plan; those calls then require the same device to be current
- * (BFZ_ESTATE otherwise).  Uploading again on the same device does nothing;
- * on another device it is BFZ_EINVAL.  Errors: BFZ_EINVAL, BFZ_EHIP. */
+/* Copy the plan's tile table to the current HIP device if it has no device
+ * copy yet (a plan created while no device was visible).  A plan whose table
+ * is already on the current device is left as it is (bfz_plan_create has
+ * usually done the upload); one whose table is on another device gives
+ * BFZ_EINVAL.  Errors: BFZ_EINVAL, BFZ_EHIP. */
 int bfz_plan_upload(bfz_plan* plan);
 
 /* Free the plan and its device table.  NULL is accepted. */
@@ -167,7 +182,7 @@ int pack_shard(const bfz_plan* plan, const float* const* src, float* dst, void* 
 /*
  * pack_shard into tiles dst_stride floats apart: slot s is written at
  * dst + s * dst_stride (pack_shard is dst_stride = 16384).  Folds master,
- * m or v into a strided state layout (bfz_adamw.state_stride), e.g. the
+ * m or v into a strided state layout (bfz_step_options.state_stride), e.g. the
  * interleaved one, where master, m and v are dst = state, state + 16384
  * and state + 32768 with dst_stride = 49152.  dst_stride: a multiple of 4
  * in [16384, 2^26]; only the 16384 floats of each slot are written.
@@ -184,7 +199,7 @@ int pack_shard_strided(const bfz_plan* plan, const float* const* src, float* dst
  *                       p = p - (lr / (1 - b1^t)) m / (sqrt(v) / sqrt(1 - b2^t) + eps)
  *                       p = p - lr wd p          (when wd != 0; on the updated p)
  *   per tile:           amax = max |p|;  scale_inv = amax / 448 (or its power-of-two
- *                       form, see bfz_adamw.scale_pow2), or 1 when amax == 0, or
+ *                       form, see bfz_step_options.scale_pow2), or 1 when amax == 0, or
  *                       2^-149 when amax / 448 rounds to zero in FP32
  *                       (0 < amax <= 224 * 2^-149: subnormal tiles)
  *   per element:        code = E4M3(p / scale_inv), 0 in an all-zero tile,
@@ -194,10 +209,11 @@ int pack_shard_strided(const bfz_plan* plan, const float* const* src, float* dst
  * are formed in double on the host and rounded once to FP32; every element
  * operation is a single IEEE binary32 operation (no fused multiply-add,
  * correctly rounded sqrt and divide).
- * master, m, v: read and overwritten in place (16-byte aligned); tile s
- * of each at s * hp->state_stride floats (16384 when 0).
+ * master, m, v: three tile-major arrays of n_tiles * 16384 floats, read
+ * and overwritten in place (16-byte aligned).
  * grad: read only (16-byte aligned).  codes: n_tiles * 16384 bytes written
  * (16-byte aligned).  scale_inv: n_tiles floats written (4-byte aligned).
+ * hp: the 48-byte bfz_adamw, read during the call only.
  * n_tiles = 0 is a no-op; at most 4,194,303 tiles per call (one 1024-thread
  * workgroup per tile, and a launch counts its work-items in 32 bits).
  * Padding tiles (all zero) stay zero and give scale_inv 1 and codes 0.
@@ -206,6 +222,16 @@ int pack_shard_strided(const bfz_plan* plan, const float* const* src, float* dst
  */
 int adamw_fp8_step(float* master, const float* grad, float* m, float* v, uint8_t* codes,
                    float* scale_inv, int64_t n_tiles, const bfz_adamw* hp, void* stream);
+
+/*
+ * adamw_fp8_step with options (opts NULL: the defaults, which is exactly
+ * adamw_fp8_step): power-of-two tile scales, and master / m / v tiles
+ * opts->state_stride floats apart (tile s of each at s * stride).
+ * Errors: as adamw_fp8_step, and BFZ_EINVAL for bad options.
+ */
+int adamw_fp8_step_ex(float* master, const float* grad, float* m, float* v, uint8_t* codes,
+                      float* scale_inv, int64_t n_tiles, const bfz_adamw* hp,
+                      const bfz_step_options* opts, void* stream);
 
 /*
  * pack_shard of the gradients and adamw_fp8_step in one pass: the same
@@ -219,19 +245,20 @@ int adamw_fp8_step(float* master, const float* grad, float* m, float* v, uint8_t
  * gradients (NULL allowed for weights the rank does not touch; 4-byte
  * alignment is enough, a 16-byte aligned weight whose W is a multiple of 4
  * takes the vector path).  master, m, v: q tiles in the shard layout
- * (tile s at s * hp->state_stride floats, 16384 when 0), updated in
- * place; codes: q * 16384 bytes; scale_inv: q floats.
+ * (tile s at s * opts->state_stride floats, 16384 when 0 or opts is
+ * NULL), updated in place; codes: q * 16384 bytes; scale_inv: q floats.
+ * opts: as in adamw_fp8_step_ex (NULL: defaults).
  * Padding slots must hold zero state; their gradient is taken as zero.
  * Errors: BFZ_EINVAL, BFZ_EALIGN, BFZ_ESTATE, BFZ_EHIP.
  */
 int fold_adamw_fp8_step(const bfz_plan* plan, const float* const* grad, float* master, float* m,
                         float* v, uint8_t* codes, float* scale_inv, const bfz_adamw* hp,
-                        void* stream);
+                        const bfz_step_options* opts, void* stream);
 
 /*
  * fold_adamw_fp8_step and unpack_fp8 in one pass: the same results, bit for
  * bit, as
- *     fold_adamw_fp8_step(plan, grad, master, m, v, codes, scale_inv, hp, stream);
+ *     fold_adamw_fp8_step(plan, grad, master, m, v, codes, scale_inv, hp, opts, stream);
  *     unpack_fp8(plan, codes, scale_inv, dst_fp8, dst_scale, stream);
  * with each tile's codes and scale written straight into the row-major FP8
  * weight and scale grid from the registers that produced them (the unfold
@@ -248,17 +275,18 @@ int fold_adamw_fp8_step(const bfz_plan* plan, const float* const* grad, float* m
 int fold_adamw_fp8_step_unpack(const bfz_plan* plan, const float* const* grad, float* master,
                                float* m, float* v, uint8_t* codes, float* scale_inv,
                                uint8_t* const* dst_fp8, float* const* dst_scale,
-                               const bfz_adamw* hp, void* stream);
+                               const bfz_adamw* hp, const bfz_step_options* opts, void* stream);
 
 /*
  * fold_adamw_fp8_step_unpack with power-of-two scales, plus the transposed
  * copy of bfz_transpose_pow2, in one pass: the same results, bit for bit, as
  *     fold_adamw_fp8_step_unpack(plan, grad, master, m, v, codes, scale_inv,
- *                                dst_fp8, dst_scale, hp, stream);
+ *                                dst_fp8, dst_scale, hp, opts, stream);
  *     bfz_transpose_pow2(plan, codes, scale_inv, dst_t, dst_t_scale, stream);
  * with W^T built from the step's codes in LDS instead of read back ("FP8-Flow-
  * MoE", section 3.1: the column-wise copy the backward pass reads, made by
- * exponent edits only).  hp->scale_pow2 must be set (BFZ_EINVAL otherwise).
+ * exponent edits only).  opts->scale_pow2 must be set (BFZ_EINVAL
+ * otherwise, NULL opts included).
  * dst_t / dst_t_scale: as in bfz_transpose_pow2.  codes and scale_inv may
  * both be NULL (no tile-major copy).  Other arguments as in
  * fold_adamw_fp8_step_unpack.
@@ -268,7 +296,8 @@ int fold_adamw_fp8_step_unpack_t(const bfz_plan* plan, const float* const* grad,
                                  float* m, float* v, uint8_t* codes, float* scale_inv,
                                  uint8_t* const* dst_fp8, float* const* dst_scale,
                                  uint8_t* const* dst_t, float* const* dst_t_scale,
-                                 const bfz_adamw* hp, void* stream);
+                                 const bfz_adamw* hp, const bfz_step_options* opts,
+                                 void* stream);
 
 /*
  * Unfold of the rank's owned slots: dst_fp8[p][e][128 i + a][128 j + b] =
@@ -289,7 +318,8 @@ int unpack_fp8(const bfz_plan* plan, const uint8_t* codes, const float* scale_in
 /*
  * Scaling-aware transpose ("FP8-Flow-MoE", section 3.1, direct transpose):
  * the transposed copy W^T of the rank's tiles, re-quantized by exponent
- * edits only.  Input: codes and scales of a step run with scale_pow2 (every
+ * edits only.  Input: codes and scales of a step run with
+ * bfz_step_options.scale_pow2 (every
  * scale_inv a power of two; other scales give unspecified results).
  * Output, for every owned tile (i, j) of weight p, expert e:
  *   dst_t[p][e][128 j + c][128 i + r]   (W^T, row-major [E, W, H])

@@ -27,9 +27,15 @@
 #include "bfz_internal.h"
 
 // ---- the HIP runtime calls of the host code, on host memory ----------------
-static int g_device = 0;  // the "current device" the host code sees
+static int g_device = 0;        // the "current device" the host code sees
+static int g_device_count = 1;  // 0: a host with no HIP device
 extern "C" {
+hipError_t hipGetDeviceCount(int* n) {
+    *n = g_device_count;
+    return g_device_count > 0 ? hipSuccess : hipErrorNoDevice;
+}
 hipError_t hipGetDevice(int* d) {
+    if (g_device_count == 0) return hipErrorNoDevice;
     *d = g_device;
     return hipSuccess;
 }
@@ -326,13 +332,26 @@ void run_plan_case(const std::vector<int64_t>& dims, int32_t D) {
               "plan_tile range");
         seen += owned;
 
-        // the calls before upload report a state error
-        std::vector<const float*> nul(size_t(n), nullptr);
-        float* tiny_dst = exact<float>(kTileElems * (q > 0 ? q : 1));
-        CHECK(pack_shard(plan, nul.data(), tiny_dst, nullptr) == BFZ_ESTATE, "pack before upload");
-        std::free(tiny_dst);
-        CHECK(bfz_plan_upload(plan) == BFZ_OK, "upload: %s", bfz_last_error());
-        CHECK(bfz_plan_upload(plan) == BFZ_OK, "second upload on the same device");
+        // created with a device visible, the plan already holds its device
+        // table: uploading again changes nothing
+        CHECK(bfz_plan_upload(plan) == BFZ_OK, "upload on the same device: %s", bfz_last_error());
+        {   // a plan created on a host without a device is host-only: its
+            // device calls report a state error until bfz_plan_upload
+            g_device_count = 0;
+            bfz_plan* host_only = nullptr;
+            CHECK(bfz_plan_create(dims.data(), n, D, rank, &host_only) == BFZ_OK, "host-only plan: %s",
+                  bfz_last_error());
+            g_device_count = 1;
+            std::vector<const float*> nul(size_t(n), nullptr);
+            float* tiny_dst = exact<float>(kTileElems * (q > 0 ? q : 1));
+            CHECK(pack_shard(host_only, nul.data(), tiny_dst, nullptr) == BFZ_ESTATE &&
+                      std::strstr(bfz_last_error(), "no device table"),
+                  "pack with a host-only plan");
+            CHECK(bfz_plan_upload(host_only) == BFZ_OK, "upload of a host-only plan: %s", bfz_last_error());
+            CHECK(bfz_plan_upload(host_only) == BFZ_OK, "second upload on the same device");
+            std::free(tiny_dst);
+            bfz_plan_destroy(host_only);
+        }
 
         // exact-size weights, FP8 weights, scale grids and transposes
         std::vector<float*> wts(size_t(n), nullptr), grads(size_t(n), nullptr);
@@ -416,35 +435,51 @@ void run_plan_case(const std::vector<int64_t>& dims, int32_t D) {
                               w8[size_t(r[0])][(r[1] * H + 128 * r[2] + a) * W + 128 * r[3] + b],
                           "transposed element");
         }
-        // the step entry points reach every slot of the shard
-        bfz_adamw hp{1e-4, 0.9, 0.95, 1e-8, 0.1, 1, 0, 0};
+        // the step entry points reach every slot of the shard; the
+        // hyper-parameters (exactly the six-field, 48-byte struct) and
+        // the options sit in heap blocks of their exact size, so reading past
+        // either is a sanitizer report
+        bfz_adamw* hpp = exact<bfz_adamw>(1);
+        *hpp = bfz_adamw{1e-4, 0.9, 0.95, 1e-8, 0.1, 1};
+        const bfz_adamw& hp = *hpp;
+        bfz_step_options* opt = exact<bfz_step_options>(1);
+        *opt = bfz_step_options{0, 0, 0};
         g_calls.clear();
         CHECK(adamw_fp8_step(shard, shard, m, v, codes, sc, q, &hp, nullptr) == BFZ_OK, "step: %s", bfz_last_error());
+        CHECK(adamw_fp8_step_ex(shard, shard, m, v, codes, sc, q, &hp, opt, nullptr) == BFZ_OK, "step ex: %s",
+              bfz_last_error());
+        CHECK(adamw_fp8_step_ex(shard, shard, m, v, codes, sc, q, &hp, nullptr, nullptr) == BFZ_OK,
+              "step ex, no options: %s", bfz_last_error());
         g_calls.clear();
         CHECK(fold_adamw_fp8_step(plan, const_cast<const float* const*>(grads.data()), shard, m, v, codes, sc, &hp,
-                                  nullptr) == BFZ_OK,
+                                  nullptr, nullptr) == BFZ_OK,
               "fold step: %s", bfz_last_error());
         check_segments(plan, q, false, "fold_adamw_fp8_step");
         CHECK(fold_adamw_fp8_step_unpack(plan, const_cast<const float* const*>(grads.data()), shard, m, v, codes, sc,
-                                         w8.data(), grid.data(), &hp, nullptr) == BFZ_OK,
+                                         w8.data(), grid.data(), &hp, opt, nullptr) == BFZ_OK,
               "one-kernel step: %s", bfz_last_error());
         check_segments(plan, q, false, "fold_adamw_fp8_step_unpack");
         CHECK(fold_adamw_fp8_step_unpack(plan, const_cast<const float* const*>(grads.data()), shard, m, v, nullptr,
-                                         nullptr, w8.data(), grid.data(), &hp, nullptr) == BFZ_OK,
+                                         nullptr, w8.data(), grid.data(), &hp, nullptr, nullptr) == BFZ_OK,
               "one-kernel step without tile-major codes: %s", bfz_last_error());
         check_segments(plan, q, false, "fold_adamw_fp8_step_unpack (row-major only)");
-        bfz_adamw hp2 = hp;
         CHECK(fold_adamw_fp8_step_unpack_t(plan, const_cast<const float* const*>(grads.data()), shard, m, v,
-                                           codes, sc, w8.data(), grid.data(), wt8.data(), tgrid.data(), &hp2,
+                                           codes, sc, w8.data(), grid.data(), wt8.data(), tgrid.data(), &hp, opt,
                                            nullptr) == BFZ_EINVAL,
               "transposed copy without power-of-two scales");
-        g_calls.clear();
-        hp2.scale_pow2 = 1;
         CHECK(fold_adamw_fp8_step_unpack_t(plan, const_cast<const float* const*>(grads.data()), shard, m, v,
-                                           codes, sc, w8.data(), grid.data(), wt8.data(), tgrid.data(), &hp2,
+                                           codes, sc, w8.data(), grid.data(), wt8.data(), tgrid.data(), &hp,
+                                           nullptr, nullptr) == BFZ_EINVAL,
+              "transposed copy without options");
+        g_calls.clear();
+        opt->scale_pow2 = 1;
+        CHECK(fold_adamw_fp8_step_unpack_t(plan, const_cast<const float* const*>(grads.data()), shard, m, v,
+                                           codes, sc, w8.data(), grid.data(), wt8.data(), tgrid.data(), &hp, opt,
                                            nullptr) == BFZ_OK,
               "one-kernel step with the transposed copy: %s", bfz_last_error());
         check_segments(plan, q, false, "fold_adamw_fp8_step_unpack_t");
+        std::free(hpp);
+        std::free(opt);
 
         // a launch failure surfaces as BFZ_EHIP with a message
         if (q > 0) {
@@ -486,7 +521,6 @@ void run_layout_case(const std::vector<int64_t>& dims, int32_t D) {
         bfz_plan* plan = nullptr;
         CHECK(bfz_plan_create(dims.data(), n, D, rank, &plan) == BFZ_OK, "plan_create: %s", bfz_last_error());
         if (!plan) return;
-        CHECK(bfz_plan_upload(plan) == BFZ_OK, "upload");
         const int64_t q = bfz_plan_shard_tiles(plan), ne = q * kTileElems;
         const size_t nw = size_t(n);
         std::vector<float*> w(nw), gr(nw);
@@ -532,26 +566,28 @@ void run_layout_case(const std::vector<int64_t>& dims, int32_t D) {
                   bfz_last_error());
         CHECK(pack_shard(plan, gc, grad, nullptr) == BFZ_OK, "pack grad");
         g_calls.clear();
-        bfz_adamw hs{1e-4, 0.9, 0.95, 1e-8, 0.1, 1, 0, 0};
-        bfz_adamw hi = hs;
-        hi.state_stride = S;
+        const bfz_adamw hp{1e-4, 0.9, 0.95, 1e-8, 0.1, 1};
+        bfz_step_options hs{0, 0, 0};
+        bfz_step_options hi{0, 0, S};
         float *Pi = state, *Mi = state + kTileElems, *Vi = state + 2 * kTileElems;
-        CHECK(adamw_fp8_step(P, grad, M, V, ca, sa, q, &hs, nullptr) == BFZ_OK, "step");
-        CHECK(adamw_fp8_step(Pi, grad, Mi, Vi, cb, sb, q, &hi, nullptr) == BFZ_OK, "step interleaved: %s",
+        CHECK(adamw_fp8_step(P, grad, M, V, ca, sa, q, &hp, nullptr) == BFZ_OK, "step");
+        CHECK(adamw_fp8_step_ex(Pi, grad, Mi, Vi, cb, sb, q, &hp, &hi, nullptr) == BFZ_OK, "step interleaved: %s",
               bfz_last_error());
-        CHECK(fold_adamw_fp8_step(plan, gc, P, M, V, ca, sa, &hs, nullptr) == BFZ_OK, "fold step");
-        CHECK(fold_adamw_fp8_step(plan, gc, Pi, Mi, Vi, cb, sb, &hi, nullptr) == BFZ_OK, "fold step interleaved");
-        CHECK(fold_adamw_fp8_step_unpack(plan, gc, P, M, V, ca, sa, w8a.data(), ga.data(), &hs, nullptr) == BFZ_OK,
+        CHECK(fold_adamw_fp8_step(plan, gc, P, M, V, ca, sa, &hp, &hs, nullptr) == BFZ_OK, "fold step");
+        CHECK(fold_adamw_fp8_step(plan, gc, Pi, Mi, Vi, cb, sb, &hp, &hi, nullptr) == BFZ_OK,
+              "fold step interleaved");
+        CHECK(fold_adamw_fp8_step_unpack(plan, gc, P, M, V, ca, sa, w8a.data(), ga.data(), &hp, &hs, nullptr) ==
+                  BFZ_OK,
               "one-kernel step");
-        CHECK(fold_adamw_fp8_step_unpack(plan, gc, Pi, Mi, Vi, cb, sb, w8b.data(), gb.data(), &hi, nullptr) ==
+        CHECK(fold_adamw_fp8_step_unpack(plan, gc, Pi, Mi, Vi, cb, sb, w8b.data(), gb.data(), &hp, &hi, nullptr) ==
                   BFZ_OK,
               "one-kernel step interleaved");
         hs.scale_pow2 = hi.scale_pow2 = 1;
         CHECK(fold_adamw_fp8_step_unpack_t(plan, gc, P, M, V, ca, sa, w8a.data(), ga.data(), wta.data(),
-                                           tga.data(), &hs, nullptr) == BFZ_OK,
+                                           tga.data(), &hp, &hs, nullptr) == BFZ_OK,
               "transposed-copy step");
         CHECK(fold_adamw_fp8_step_unpack_t(plan, gc, Pi, Mi, Vi, cb, sb, w8b.data(), gb.data(), wtb.data(),
-                                           tgb.data(), &hi, nullptr) == BFZ_OK,
+                                           tgb.data(), &hp, &hi, nullptr) == BFZ_OK,
               "transposed-copy step interleaved");
         g_calls.clear();
         for (int64_t sl = 0; sl < q; ++sl) {
@@ -601,8 +637,7 @@ void run_error_paths() {
     CHECK(bfz_paramwise_split(dims, 1, 2, bop, be) == BFZ_OK && be[bop[0]] == 200 * 130, "paramwise");
 
     CHECK(bfz_plan_create(dims, 1, 1, 0, &plan) == BFZ_OK && plan, "plan");
-    CHECK(bfz_plan_upload(plan) == BFZ_OK, "upload");
-    {   // the plan belongs to the device it was uploaded on
+    {   // the plan belongs to the device it was created (uploaded) on
         const int64_t qq = bfz_plan_shard_tiles(plan);
         float* d = exact<float>(qq * kTileElems);
         float* wv = exact<float>(200 * 130);
@@ -622,7 +657,7 @@ void run_error_paths() {
     float* w = exact<float>(200 * 130 + 1);
     uint8_t* w8 = exact<uint8_t>(200 * 130 + 1);
     float* g = exact<float>(2 * 2 + 1);
-    bfz_adamw hp{1e-4, 0.9, 0.95, 1e-8, 0.1, 1, 0, 0};
+    const bfz_adamw hp{1e-4, 0.9, 0.95, 1e-8, 0.1, 1};
     const float* src[1] = {w};
     const float* src_odd[1] = {reinterpret_cast<const float*>(reinterpret_cast<const char*>(w) + 2)};
     uint8_t* d8[1] = {w8};
@@ -647,20 +682,27 @@ void run_error_paths() {
     CHECK(adamw_fp8_step(a, a, a, a, c, s, q, &bad, nullptr) == BFZ_EINVAL, "beta1 = 1");
     bad = hp;
     bad.lr = std::nan("");
-    CHECK(fold_adamw_fp8_step(plan, src, a, a, a, c, s, &bad, nullptr) == BFZ_EINVAL, "NaN lr");
+    CHECK(fold_adamw_fp8_step(plan, src, a, a, a, c, s, &bad, nullptr, nullptr) == BFZ_EINVAL, "NaN lr");
     bad = hp;
     bad.eps = -1.0;
-    CHECK(fold_adamw_fp8_step(plan, src, a, a, a, c, s, &bad, nullptr) == BFZ_EINVAL, "eps < 0");
-    CHECK(fold_adamw_fp8_step_unpack(plan, src, a, a, a, c, nullptr, d8, dg, &hp, nullptr) == BFZ_EINVAL,
+    CHECK(fold_adamw_fp8_step(plan, src, a, a, a, c, s, &bad, nullptr, nullptr) == BFZ_EINVAL, "eps < 0");
+    bad.eps = 0.0;
+    CHECK(adamw_fp8_step(a, a, a, a, c, s, q, &bad, nullptr) == BFZ_EINVAL && std::strstr(bfz_last_error(), "eps > 0"),
+          "eps = 0");
+    CHECK(fold_adamw_fp8_step_unpack(plan, src, a, a, a, c, nullptr, d8, dg, &hp, nullptr, nullptr) == BFZ_EINVAL,
           "codes without scale_inv");
-    CHECK(fold_adamw_fp8_step_unpack(plan, src, a, a, a, nullptr, nullptr, d8, dg_odd, &hp, nullptr) == BFZ_EALIGN,
+    CHECK(fold_adamw_fp8_step_unpack(plan, src, a, a, a, nullptr, nullptr, d8, dg_odd, &hp, nullptr, nullptr) ==
+              BFZ_EALIGN,
           "misaligned scale grid");
     CHECK(bfz_e4m3_encode(nullptr, c, 4, nullptr) == BFZ_EINVAL && bfz_e4m3_encode(a, c, -1, nullptr) == BFZ_EINVAL,
           "encode args");
-    bad = hp;
+    const bfz_step_options reserved{0, 1, 0};
+    CHECK(adamw_fp8_step_ex(a, a, a, a, c, s, q, &hp, &reserved, nullptr) == BFZ_EINVAL &&
+              std::strstr(bfz_last_error(), "reserved"),
+          "reserved option field");
     for (int64_t stride : {int64_t(-16384), int64_t(16383), int64_t(16386), (int64_t(1) << 26) + 4}) {
-        bad.state_stride = stride;
-        CHECK(adamw_fp8_step(a, a, a, a, c, s, q, &bad, nullptr) == BFZ_EINVAL &&
+        const bfz_step_options so{0, 0, stride};
+        CHECK(adamw_fp8_step_ex(a, a, a, a, c, s, q, &hp, &so, nullptr) == BFZ_EINVAL &&
                   std::strstr(bfz_last_error(), "state_stride"),
               "bad state_stride %lld", (long long)stride);
         CHECK(pack_shard_strided(plan, src, a, stride, nullptr) == BFZ_EINVAL, "bad dst_stride %lld",

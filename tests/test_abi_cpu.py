@@ -38,7 +38,7 @@ def test_plan_matches_oracle_plan():
         D = int(rng.integers(1, 10))
         for r in range(D):
             q, owned, table = oracle.plan(dims, D, r)
-            p = bfz.Plan(dims, D, r, upload=False)
+            p = bfz.Plan(dims, D, r)
             assert (p.shard_tiles, p.owned_tiles, p.total_tiles) == (q, owned, oracle.total_tiles(dims))
             assert np.array_equal(p.table(), table)
             if q:
@@ -51,7 +51,7 @@ def test_plan_of_the_workloads():
     for f in WL.ALL:
         w = f()
         q, owned, table = oracle.plan(w.dims, w.D, w.rank)
-        p = bfz.Plan(w.dims, w.D, w.rank, upload=False)
+        p = bfz.Plan(w.dims, w.D, w.rank)
         assert p.shard_tiles == q and p.owned_tiles == owned
         assert np.array_equal(p.table(), table), w.name
 
@@ -88,14 +88,28 @@ def test_paramwise_split_matches_oracle():
 ])
 def test_plan_rejects_bad_arguments(dims, D, rank):
     with pytest.raises(bfz.BfzError) as e:
-        bfz.Plan(dims, D, rank, upload=False)
+        bfz.Plan(dims, D, rank)
     assert e.value.code == bfz.BFZ_EINVAL
     assert bfz.lib().bfz_last_error()
 
 
-def _call_step(ptrs, n_tiles=1, hp=None):
+def _call_step(ptrs, n_tiles=1, hp=None, opts=None):
+    """adamw_fp8_step (opts None) or adamw_fp8_step_ex on fake pointers."""
     hp = hp or bfz.AdamW(lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1)
-    return bfz.lib().adamw_fp8_step(*[C.c_void_p(p) for p in ptrs], n_tiles, C.byref(hp), None)
+    args = [C.c_void_p(p) for p in ptrs]
+    if opts is None:
+        return bfz.lib().adamw_fp8_step(*args, n_tiles, C.byref(hp), None)
+    return bfz.lib().adamw_fp8_step_ex(*args, n_tiles, C.byref(hp), C.byref(opts), None)
+
+
+def test_struct_sizes_match_the_header():
+    """bfz_adamw is the six-field, 48-byte struct every step call reads;
+    the options live in the 16-byte bfz_step_options."""
+    assert C.sizeof(bfz.AdamW) == 48 and C.sizeof(bfz.StepOptions) == 16
+    text = open(os.path.join(ROOT, "include", "bfz.h")).read()
+    body = re.search(r"typedef struct \{([^}]*)\} bfz_adamw;", text).group(1)
+    assert re.sub(r"\s+", " ", body).strip() == \
+        "double lr, beta1, beta2, eps, weight_decay; int64_t step;"
 
 
 def test_step_argument_errors_without_gpu():
@@ -112,11 +126,15 @@ def test_step_argument_errors_without_gpu():
     bad = list(ok)
     bad[5] += 2
     assert _call_step(bad) == bfz.BFZ_EALIGN
-    for field, val in (("beta1", 1.0), ("beta2", -0.1), ("eps", -1.0), ("lr", float("nan")),
-                       ("step", 0), ("weight_decay", float("inf"))):
+    for field, val in (("beta1", 1.0), ("beta2", -0.1), ("eps", -1.0), ("eps", 0.0),
+                       ("lr", float("nan")), ("step", 0), ("weight_decay", float("inf"))):
         hp = bfz.AdamW(lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1)
         setattr(hp, field, val)
         assert _call_step(ok, hp=hp) == bfz.BFZ_EINVAL, field
+        assert _call_step(ok, hp=hp, opts=bfz.StepOptions()) == bfz.BFZ_EINVAL, field
+    assert "eps > 0" in bfz.lib().bfz_last_error().decode()
+    assert _call_step(ok, opts=bfz.StepOptions(reserved=1)) == bfz.BFZ_EINVAL
+    assert "reserved" in bfz.lib().bfz_last_error().decode()
 
 
 @pytest.mark.parametrize("stride", [-16384, 1, 16383, 16386, 49150, (1 << 26) + 4, 1 << 40])
@@ -124,12 +142,10 @@ def test_bad_state_stride_is_rejected_without_gpu(stride):
     """state_stride: 0, or a multiple of 4 in [16384, 2^26] (tiles of
     master / m / v may not overlap and must stay 16-byte aligned)."""
     ok = [0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000]
-    hp = bfz.AdamW(lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1,
-                   state_stride=stride)
-    assert _call_step(ok, hp=hp) == bfz.BFZ_EINVAL
+    assert _call_step(ok, opts=bfz.StepOptions(state_stride=stride)) == bfz.BFZ_EINVAL
     assert "state_stride" in bfz.lib().bfz_last_error().decode()
     L = bfz.lib()
-    p = bfz.Plan([(1, 256, 256)], 1, 0, upload=False)
+    p = bfz.Plan([(1, 256, 256)], 1, 0)
     src = (C.c_void_p * 1)(0x10000)
     assert L.pack_shard_strided(p.handle, C.cast(src, C.c_void_p), C.c_void_p(0x30000), stride,
                                 None) == bfz.BFZ_EINVAL
@@ -139,18 +155,17 @@ def test_bad_state_stride_is_rejected_without_gpu(stride):
 
 def test_good_state_stride_passes_the_checks():
     """Valid strides get past their check: pack_shard_strided stops at the
-    plan (not uploaded: BFZ_ESTATE), and a step whose only fault is beta1 = 1
-    reports that, not the stride."""
+    plan (no device here, so no device table: BFZ_ESTATE), and a step whose
+    only fault is beta1 = 1 reports that, not the stride."""
     L = bfz.lib()
-    p = bfz.Plan([(1, 256, 256)], 1, 0, upload=False)
+    p = bfz.Plan([(1, 256, 256)], 1, 0)
     src = (C.c_void_p * 1)(0x10000)
     ok = [0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000]
     for stride in (0, 16384, 49152, 1 << 26):
         assert L.pack_shard_strided(p.handle, C.cast(src, C.c_void_p), C.c_void_p(0x30000),
                                     stride or 16384, None) == bfz.BFZ_ESTATE
-        hp = bfz.AdamW(lr=1e-4, beta1=1.0, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1,
-                       state_stride=stride)
-        assert _call_step(ok, hp=hp) == bfz.BFZ_EINVAL
+        hp = bfz.AdamW(lr=1e-4, beta1=1.0, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1)
+        assert _call_step(ok, hp=hp, opts=bfz.StepOptions(state_stride=stride)) == bfz.BFZ_EINVAL
         msg = L.bfz_last_error().decode()
         assert "beta" in msg and "state_stride" not in msg, msg
     p.close()
@@ -158,9 +173,9 @@ def test_good_state_stride_passes_the_checks():
 
 def test_pack_unpack_errors_without_gpu():
     L = bfz.lib()
-    p = bfz.Plan([(1, 256, 256), (1, 128, 128)], 2, 0, upload=False)
+    p = bfz.Plan([(1, 256, 256), (1, 128, 128)], 2, 0)
     src = (C.c_void_p * 2)(0x10000, 0x20000)
-    # not uploaded
+    # no HIP device in this container: the plan has no device table
     assert L.pack_shard(p.handle, C.cast(src, C.c_void_p), C.c_void_p(0x30000), None) == bfz.BFZ_ESTATE
     assert L.pack_shard(p.handle, None, C.c_void_p(0x30000), None) == bfz.BFZ_EINVAL
     assert L.pack_shard(None, C.cast(src, C.c_void_p), C.c_void_p(0x30000), None) == bfz.BFZ_EINVAL
@@ -169,11 +184,13 @@ def test_pack_unpack_errors_without_gpu():
                         C.cast(d8, C.c_void_p), None) == bfz.BFZ_ESTATE
     hp = bfz.AdamW(lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1)
     st = [C.c_void_p(x) for x in (0x40000, 0x50000, 0x60000, 0x70000, 0x80000)]
-    assert L.fold_adamw_fp8_step(p.handle, C.cast(src, C.c_void_p), *st, C.byref(hp),
+    assert L.fold_adamw_fp8_step(p.handle, C.cast(src, C.c_void_p), *st, C.byref(hp), None,
                                  None) == bfz.BFZ_ESTATE
-    assert L.fold_adamw_fp8_step(p.handle, None, *st, C.byref(hp), None) == bfz.BFZ_EINVAL
-    assert L.fold_adamw_fp8_step(None, C.cast(src, C.c_void_p), *st, C.byref(hp),
+    assert L.fold_adamw_fp8_step(p.handle, None, *st, C.byref(hp), None, None) == bfz.BFZ_EINVAL
+    assert L.fold_adamw_fp8_step(None, C.cast(src, C.c_void_p), *st, C.byref(hp), None,
                                  None) == bfz.BFZ_EINVAL
+    assert "no device table" in (L.pack_shard(p.handle, C.cast(src, C.c_void_p), C.c_void_p(0x30000),
+                                              None) and L.bfz_last_error().decode())
     assert L.bfz_e4m3_encode(None, C.c_void_p(0x10), 5, None) == bfz.BFZ_EINVAL
     assert L.bfz_e4m3_encode(C.c_void_p(0x10), C.c_void_p(0x10), -1, None) == bfz.BFZ_EINVAL
     assert L.bfz_plan_tile(p.handle, 99, C.cast((C.c_int64 * 6)(), C.c_void_p)) == bfz.BFZ_EINVAL

@@ -17,7 +17,7 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 def test_timed_path_does_not_load_the_oracle():
     """Only the cpu_baseline leg may load the oracle: importing bench and the
     GPU workload driver it times must leave it unloaded."""
-    code = ("import sys; import bench; import tests.gpu_run; "
+    code = ("import sys; import bench; import bench_workload; "
             "assert not any(m == 'oracle' or m.startswith('oracle.') for m in sys.modules), "
             "sorted(m for m in sys.modules if 'oracle' in m)")
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,

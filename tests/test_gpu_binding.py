@@ -1,7 +1,8 @@
-"""The binding's state-layout marshalling on the GPU: master / m / v as
-contiguous tensors or as (tiles, 16384) views of one (q, 3, 16384) tensor;
-the stride each call passes in bfz_adamw.state_stride is the views' row
-stride, and inconsistent layouts are refused before any kernel runs."""
+"""The binding's marshalling on the GPU: master / m / v as contiguous
+tensors or as (tiles, 16384) views of one (q, 3, 16384) tensor (the stride
+each call passes in bfz_step_options.state_stride is the views' row
+stride), per-weight tensors checked against the plan's shapes, and
+inconsistent arguments refused before any kernel runs."""
 import sys
 
 import numpy as np
@@ -37,9 +38,6 @@ def test_mismatched_state_strides_are_refused():
     hp = bfz.AdamW(step=1, **HP)
     with pytest.raises(ValueError, match="different tile strides"):
         bfz.adamw_fp8_step(state[:, 0], g, flat, state[:, 2], codes, sc, hp)
-    hp_bad = bfz.AdamW(step=1, state_stride=16384, **HP)
-    with pytest.raises(ValueError, match="disagrees"):
-        bfz.adamw_fp8_step(state[:, 0], g, state[:, 1], state[:, 2], codes, sc, hp_bad)
     gappy = torch.zeros(q, 2 * 16384, dtype=torch.float32, device="cuda")[:, ::2]
     with pytest.raises(TypeError):  # (q, 16384) but its elements are not contiguous within a tile
         bfz.adamw_fp8_step(gappy, g, state[:, 1], state[:, 2], codes, sc, hp)
@@ -50,9 +48,9 @@ def test_mismatched_state_strides_are_refused():
 
 
 def test_caller_hp_is_not_modified_and_layouts_agree():
-    """The same step through contiguous arrays and through interleaved views
-    gives bit-identical results; the caller's AdamW struct keeps
-    state_stride 0 (the binding passes a copy)."""
+    """The same step through contiguous arrays (adamw_fp8_step) and through
+    interleaved views (adamw_fp8_step_ex with state_stride 49152) gives
+    bit-identical results; the caller's AdamW struct is left as it was."""
     q = 5
     _say("layout agreement through the binding, q =", q)
     torch.manual_seed(3)
@@ -68,7 +66,7 @@ def test_caller_hp_is_not_modified_and_layouts_agree():
     bfz.adamw_fp8_step(*sep[:1], g, *sep[1:], codes_a, sc_a, hp)
     bfz.adamw_fp8_step(state[:, 0], g, state[:, 1], state[:, 2], codes_b, sc_b, hp)
     torch.cuda.synchronize()
-    assert hp.state_stride == 0
+    assert bytes(hp) == bytes(bfz.AdamW(step=7, **HP))
     for k in range(3):
         assert torch.equal(sep[k].view(torch.int32), state[:, k].reshape(-1).view(torch.int32)), k
     assert torch.equal(codes_a, codes_b) and torch.equal(sc_a, sc_b)
@@ -126,7 +124,7 @@ def test_gapped_state_stride(mode):
     weights that span several tiles: bit-identical to three separate
     arrays, and the gap slots are never written."""
     from synth import workloads as WL
-    from tests.gpu_run import GpuWorkload
+    from bench_workload import GpuWorkload
     w = WL.ragged()
     w.dims = w.dims[:6]
     _say("gapped state stride 65536, 6 ragged matrices, mode", mode)
@@ -144,3 +142,47 @@ def test_gapped_state_stride(mode):
     for k in a:
         assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
     assert (block[:, 3] == 7.0).all()
+
+
+def test_undersized_per_weight_tensors_are_refused():
+    """Each per-weight tensor must hold its whole row-major weight (or scale
+    grid): the kernels address it through the plan's table, so a smaller one
+    would be read or written out of bounds.  Refused with ValueError before
+    any launch, for every entry point that takes per-weight tensors."""
+    dims = [(2, 200, 300), (1, 129, 130)]
+    plan = bfz.Plan(dims, 1, 0)
+    q = plan.shard_tiles
+    _say("per-weight size checks, dims", dims, "q =", q)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    full = [E * H * W for E, H, W in dims]
+    grid = [E * -(-H // 128) * -(-W // 128) for E, H, W in dims]
+    tgrid = [E * W * -(-H // 128) for E, H, W in dims]
+    grads = [torch.zeros(n, **f32) for n in full]
+    short = [torch.zeros(200 * 300, **f32), grads[1]]   # one expert of two
+    st = [torch.zeros(q * 16384, **f32) for _ in range(3)]
+    codes = torch.zeros(q * 16384, **u8)
+    sc = torch.zeros(q, **f32)
+    d8 = [torch.zeros(n, **u8) for n in full]
+    dsc = [torch.zeros(n, **f32) for n in grid]
+    dt = [torch.zeros(n, **u8) for n in full]
+    dts = [torch.zeros(n, **f32) for n in tgrid]
+    hp = bfz.AdamW(step=1, **HP)
+    with pytest.raises(ValueError, match=r"srcs\[0\]"):
+        bfz.pack_shard(plan, short, st[0])
+    with pytest.raises(ValueError, match=r"grads\[0\]"):
+        bfz.fold_adamw_fp8_step(plan, short, *st, codes, sc, hp)
+    with pytest.raises(ValueError, match=r"dst_fp8\[1\]"):
+        bfz.unpack_fp8(plan, codes, sc, [d8[0], d8[1][:-1]], dsc)
+    with pytest.raises(ValueError, match=r"dst_scale\[0\]"):   # a grid sized W / 128, not E hb wb
+        bfz.fold_adamw_fp8_step_unpack(plan, grads, *st, codes, sc, d8,
+                                       [torch.zeros(3, **f32), dsc[1]], hp)
+    with pytest.raises(ValueError, match=r"dst_t_scale\[0\]"):
+        bfz.fold_adamw_fp8_step_unpack_t(plan, grads, *st, codes, sc, d8, dsc, dt,
+                                         [dsc[0], dts[1]], hp)
+    with pytest.raises(ValueError, match=r"dst_t\[1\]"):
+        bfz.transpose_pow2(plan, codes, sc, [dt[0], dt[1][:100]], dts)
+    with pytest.raises(ValueError, match="3 tensors for 2 weights"):
+        bfz.pack_shard(plan, grads + [grads[0]], st[0])
+    torch.cuda.synchronize()
+    assert not any(x.any() for x in st + d8 + dsc + dt + dts) and not codes.any()  # nothing ran

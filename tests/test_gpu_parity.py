@@ -18,7 +18,7 @@ import blockwise_fp8_zero_amd as bfz
 import oracle
 from synth import workloads as WL
 from tests.compare import compare
-from tests.gpu_run import GpuWorkload
+from bench_workload import GpuWorkload
 from tests.oracle_run import oracle_slots, sample_slots
 
 pytestmark = pytest.mark.gpu
@@ -313,19 +313,20 @@ def test_random_configurations(seed):
             bfz.pack_shard(plan, dev[k], st[k])
         codes = torch.empty(q * 16384, dtype=torch.uint8, device="cuda")
         sc = torch.empty(q, dtype=torch.float32, device="cuda")
-        h = bfz.AdamW(step=t, scale_pow2=int(pow2), **hp)
+        h = bfz.AdamW(step=t, **hp)
         if route == "unfused":
             gt = torch.empty(q * 16384, dtype=torch.float32, device="cuda")
             bfz.pack_shard(plan, dev["g"], gt)
-            bfz.adamw_fp8_step(st["p"], gt, st["m"], st["v"], codes, sc, h)
+            bfz.adamw_fp8_step(st["p"], gt, st["m"], st["v"], codes, sc, h, scale_pow2=pow2)
         elif route == "fused":
-            bfz.fold_adamw_fp8_step(plan, dev["g"], st["p"], st["m"], st["v"], codes, sc, h)
+            bfz.fold_adamw_fp8_step(plan, dev["g"], st["p"], st["m"], st["v"], codes, sc, h,
+                                    scale_pow2=pow2)
         else:
             d8 = [torch.zeros(int(np.prod(d)), dtype=torch.uint8, device="cuda") for d in dims]
             dsc = [torch.zeros(d[0] * -(-d[1] // 128) * -(-d[2] // 128), dtype=torch.float32,
                                device="cuda") for d in dims]
             bfz.fold_adamw_fp8_step_unpack(plan, dev["g"], st["p"], st["m"], st["v"], codes, sc,
-                                           d8, dsc, h)
+                                           d8, dsc, h, scale_pow2=pow2)
         torch.cuda.synchronize()
         gpu = dict(master=st["p"].cpu().numpy(), m=st["m"].cpu().numpy(), v=st["v"].cpu().numpy(),
                    codes=codes.cpu().numpy(), scale_inv=sc.cpu().numpy())
@@ -389,20 +390,21 @@ def test_many_weights_several_segments(pow2, layout):
             bfz.pack_shard(plan, dev[k], st[k])
         codes = torch.empty(q * 16384, dtype=torch.uint8, device="cuda")
         sc = torch.empty(q, dtype=torch.float32, device="cuda")
-        h = bfz.AdamW(step=3, scale_pow2=int(pow2), **hp)
+        h = bfz.AdamW(step=3, **hp)
         d8 = [torch.zeros(int(np.prod(d)), dtype=torch.uint8, device="cuda") for d in dims]
         dsc = [torch.zeros(osc[k].size, dtype=torch.float32, device="cuda") for k in range(len(dims))]
         if route == "unfused":
             gt = torch.empty(q * 16384, dtype=torch.float32, device="cuda")
             bfz.pack_shard(plan, dev["g"], gt)
-            bfz.adamw_fp8_step(st["p"], gt, st["m"], st["v"], codes, sc, h)
+            bfz.adamw_fp8_step(st["p"], gt, st["m"], st["v"], codes, sc, h, scale_pow2=pow2)
             bfz.unpack_fp8(plan, codes, sc, d8, dsc)
         elif route == "fused":
-            bfz.fold_adamw_fp8_step(plan, dev["g"], st["p"], st["m"], st["v"], codes, sc, h)
+            bfz.fold_adamw_fp8_step(plan, dev["g"], st["p"], st["m"], st["v"], codes, sc, h,
+                                    scale_pow2=pow2)
             bfz.unpack_fp8(plan, codes, sc, d8, dsc)
         elif route == "fused_unpack":
             bfz.fold_adamw_fp8_step_unpack(plan, dev["g"], st["p"], st["m"], st["v"], codes, sc,
-                                           d8, dsc, h)
+                                           d8, dsc, h, scale_pow2=pow2)
         else:
             dt = [torch.zeros(int(np.prod(d)), dtype=torch.uint8, device="cuda") for d in dims]
             dts = [torch.zeros(ots[k].size, dtype=torch.float32, device="cuda")
@@ -588,13 +590,14 @@ def test_subnormal_masters_and_edge_amax(pow2):
         d8 = [torch.zeros(int(np.prod(d)), dtype=torch.uint8, device="cuda") for d in dims]
         dsc = [torch.zeros(x.size, dtype=torch.float32, device="cuda") for x in odsc]
         for t in steps:
-            hp = bfz.AdamW(step=t, scale_pow2=pow2, **WL.HP)
+            hp = bfz.AdamW(step=t, **WL.HP)
             if route == "unfused":
-                bfz.adamw_fp8_step(p, gt_dev, m, v, codes, sc, hp)
+                bfz.adamw_fp8_step(p, gt_dev, m, v, codes, sc, hp, scale_pow2=pow2)
             elif route == "fused":
-                bfz.fold_adamw_fp8_step(plan, g_dev, p, m, v, codes, sc, hp)
+                bfz.fold_adamw_fp8_step(plan, g_dev, p, m, v, codes, sc, hp, scale_pow2=pow2)
             else:
-                bfz.fold_adamw_fp8_step_unpack(plan, g_dev, p, m, v, codes, sc, d8, dsc, hp)
+                bfz.fold_adamw_fp8_step_unpack(plan, g_dev, p, m, v, codes, sc, d8, dsc, hp,
+                                               scale_pow2=pow2)
         if route != "fused_unpack":
             bfz.unpack_fp8(plan, codes, sc, d8, dsc)
         torch.cuda.synchronize()

@@ -11,7 +11,7 @@ import blockwise_fp8_zero_amd as bfz
 import oracle
 from synth import workloads as WL
 from tests.compare import compare
-from tests.gpu_run import GpuWorkload
+from bench_workload import GpuWorkload
 from tests.oracle_run import oracle_slots, sample_slots
 
 pytestmark = pytest.mark.gpu
