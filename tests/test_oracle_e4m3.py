@@ -73,12 +73,10 @@ def _chunk_mismatches(ora, start, n, stride=1):
 
 @pytest.mark.slow
 def test_encode_exhaustive_vs_torch(ora):
-    """Every non-negative fp32 pattern (2^31) and every 7th negative one;
-    non-finite patterns skipped.  The sign is one bit copied through, so the
-    negative half is sampled densely rather than walked whole."""
+    """Every one of the 2^32 fp32 bit patterns against torch's float8_e4m3fn
+    cast after clamping to +-448; non-finite patterns skipped."""
     chunk = 1 << 26
-    starts = [(s, 1) for s in range(0, 1 << 31, chunk)]
-    starts += [(s, 7) for s in range(1 << 31, 1 << 32, chunk)]
+    starts = [(s, 1) for s in range(0, 1 << 32, chunk)]
     n_thr = torch.get_num_threads()
     torch.set_num_threads(1)
     try:
