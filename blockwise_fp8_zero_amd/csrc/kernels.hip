@@ -139,6 +139,24 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t n_tiles) {
     return j < per ? x * per + j : 8 * per + x;
 }
 
+// The step kernels' order: runs of kStepRun consecutive tiles per XCD,
+// dealt round-robin, so the workgroups in flight cover one compact window
+// of consecutive tiles (dispatch order) while each XCD's L2 still sees
+// neighbouring tiles -- whose row-major gradient rows and code rows share
+// DRAM pages -- back to back.  Workgroup b = 8 j + x (XCD x) takes tile
+// 8 R (j / R) + R x + j % R; the last n % (8 R) tiles keep their own index.
+// Bijective for any n_tiles.  Measured against the XCD-contiguous order
+// (xcd_tile), one-kernel step, same process: 2.01B-element shard 9.75 ->
+// 9.58 ms, dense 3.92 -> 3.88, MoE 1.71 -> 1.69, ragged 0.366 -> 0.359
+// (runs of 2 within 0.5% of 4; 8 and 16 slower; plain order in between).
+constexpr int64_t kStepRun = 4;
+__device__ __forceinline__ int64_t step_tile_of(int64_t b, int64_t n_tiles) {
+    const int64_t full = n_tiles / (8 * kStepRun) * (8 * kStepRun);
+    if (b >= full) return b;
+    const int64_t x = b % 8, j = b / 8;
+    return (j / kStepRun) * (8 * kStepRun) + x * kStepRun + j % kStepRun;
+}
+
 // One 1024-thread workgroup (16 wave64s) owns one tile: each thread holds
 // 4 float4 of it (float4 i = k * 1024 + thread, k < 4, i.e. rows
 // 32 k + thread / 32, columns 4 (thread % 32) .. +3).  The source issues a
@@ -400,7 +418,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(
     float* __restrict__ mom2, uint32_t* __restrict__ codes, float* __restrict__ scale_inv,
     StepScalars s, int64_t n_tiles) {
     extern __shared__ float wave_amax[];
-    const int64_t tile = xcd_tile(blockIdx.x, n_tiles);
+    const int64_t tile = step_tile_of(blockIdx.x, n_tiles);
     const TileMajorGrad g{TileBlock(grad + tile * kTileElems, kTileElems * 4)};
     step_tile(tile, master, mom1, mom2, codes, scale_inv, s, g, wave_amax);
 }
@@ -413,7 +431,7 @@ __global__ __launch_bounds__(kStepThreads) void fold_step_kernel(
     float* __restrict__ mom1, float* __restrict__ mom2, uint32_t* __restrict__ codes,
     float* __restrict__ scale_inv, StepScalars s, int64_t n_slots) {
     extern __shared__ float wave_amax[];
-    const int64_t slot = xcd_tile(blockIdx.x, n_slots);
+    const int64_t slot = step_tile_of(blockIdx.x, n_slots);
     const TileEntry t = entries[slot];
     with_row_major_grad(t, grads, [&](const auto& g) {
         step_tile(slot, master, mom1, mom2, codes, scale_inv, s, g, wave_amax);
@@ -428,7 +446,7 @@ __global__ __launch_bounds__(kStepThreads) void fold_step_unfold_kernel(
     float* __restrict__ master, float* __restrict__ mom1, float* __restrict__ mom2,
     uint32_t* __restrict__ codes, float* __restrict__ scale_inv, StepScalars s, int64_t n_slots) {
     extern __shared__ float wave_amax[];
-    const int64_t slot = xcd_tile(blockIdx.x, n_slots);
+    const int64_t slot = step_tile_of(blockIdx.x, n_slots);
     const TileEntry t = entries[slot];
     RowMajorCodes out{nullptr, nullptr, t.ld, t.valid_rows, t.valid_cols, false};
     if (t.local >= 0) {
@@ -803,7 +821,7 @@ __global__ __launch_bounds__(kStepThreads) void fold_step_unfold_t_kernel(
     float* wave_amax = smem;                                       // kStepWaves floats
     uint32_t* tile_rm = reinterpret_cast<uint32_t*>(smem + 64);    // 16 KiB, codes by rows
     uint32_t* tile_t = tile_rm + kTileElems / 4;                   // 16 KiB, codes by W^T rows
-    const int64_t slot = xcd_tile(blockIdx.x, n_slots);
+    const int64_t slot = step_tile_of(blockIdx.x, n_slots);
     const TileEntry t = entries[slot];
     StagedCodes out{RowMajorCodes{nullptr, nullptr, t.ld, t.valid_rows, t.valid_cols, false}, nullptr,
                     tile_rm};
