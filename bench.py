@@ -18,22 +18,30 @@ The split itself (the planner) runs once at set-up.
       write stream;
   separate: three tile-major arrays.
 
-Default workload: the dense-LLM rank shard -- 32 layers x {4 of 4096x4096,
-2 of 4096x11008, 1 of 11008x4096}, D = 8, rank 0: 49408 tiles, 809.5M
-elements.  Its moments are warm from 10 prior steps (t = 1..10, fresh
-N(0, 1e-3) grads each); the timed steps continue at t = 11, 12, ... on the
-t = 11 gradients, which stay resident in HBM (inputs are never re-drawn
-inside the timed region).
+Default workload (the headline): the large shard -- 120 matrices of
+4096x4096, 2.01B elements, D = 1, step t = 1000, 1% of the tiles all zero;
+every output is written: the tile-major codes and scale_inv and the
+row-major FP8 weights and scale grids.  Its inputs stay resident in HBM:
+the timed steps continue at t = 1000, 1001, ... on the t = 1000 gradients
+(never re-drawn inside the timed region).
 
 Output: one JSON line.  value = shard elements per second of the whole
-step.  roofline = the step kernel's algorithmic HBM bytes per launch
-(29 B per element + 4 B per tile, plus 1 B per element + 4 B per tile for
-the row-major codes and scales in the one-kernel path; gradient reads and
-row-major writes count valid elements) over its mean launch time, measured
-with HIP events on the stream the kernels run on.  pack / unpack = the fold
-and the unfold timed the same way where they run as passes of their own
-(unfused / fused routes).  cpu_baseline = the C oracle on a bounded sample
-of the same workload, on the host's cores.
+step (padded elements; on the headline workload every element is valid).
+roofline = the step kernel's algorithmic HBM bytes per step (master, m, v
+read and written: 24 B per element; the gradient read: 4 B per valid
+element; the tile-major code: 1 B per element; scale_inv: 4 B per tile; the
+row-major code: 1 B per valid element; the scale-grid cell: 4 B per owned
+tile) over its mean launch time, measured with HIP events on the stream the
+kernels run on.  After the timed region, outside it:
+  configs: the other shard workloads (dense-LLM, MoE experts, ragged)
+      through the same one-kernel step, each timed the same way;
+  pack / unpack: pack_shard of the gradients and unpack_fp8 of the codes
+      as passes of their own on the headline shard;
+  transpose_pow2: the scaling-aware transpose on the headline shard;
+  parity (oracle leg): sampled slots of the headline step and every slot
+      of a tiny workload compared with the C oracle, counts reported;
+  cpu_baseline (oracle leg): the C oracle on a bounded sample of the
+      headline workload, on the host's cores.
 """
 import argparse
 import hashlib
@@ -49,22 +57,19 @@ if ROOT not in sys.path:
 
 METRIC = "AdamW+blockwise-FP8 requant elems/s and HBM GB/s (% of peak) on one MI355X"
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published peak
-STEP_BYTES_PER_ELEM = 29          # read p, g, m, v (16) + write p, m, v (12) + code (1)
-STEP_BYTES_PER_TILE = 4           # scale_inv
-PACK_BYTES_PER_ELEM = 8           # read grad + write tile
-UNPACK_BYTES_PER_ELEM = 2         # read code + write code
-UNPACK_BYTES_PER_TILE = 8         # read + write scale
-TRAFFIC_FILES = {k: os.path.join(ROOT, "profiles", f"{k}_dense_llm_traffic.md")
-                 for k in ("fold_step_unfold_kernel", "fold_step_kernel", "step_kernel",
-                           "transpose_pow2_kernel", "fold_step_unfold_t_kernel")}
 KERNEL_OF_PATH = {"fused_unpack": "fold_step_unfold_kernel",
                   "fused_unpack_t": "fold_step_unfold_t_kernel", "fused": "fold_step_kernel",
                   "unfused": "step_kernel"}
 KERNEL_SRC = os.path.join(ROOT, "blockwise_fp8_zero_amd", "csrc", "kernels.hip")
+OTHER_CONFIGS = ("dense_llm", "moe_experts", "ragged")
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def traffic_file(kernel, workload):
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
 
 
 def kernel_sha():
@@ -79,10 +84,11 @@ def kernel_sha():
     return hashlib.sha256(src.encode()).hexdigest()
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from its committed rocprofv3 PMC
-    summary, if that was taken on the current kernel source; else None."""
-    path = TRAFFIC_FILES[kernel]
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch set of `kernel` on `workload` from its committed
+    rocprofv3 PMC summary, if that was taken on the current kernel source;
+    else None."""
+    path = traffic_file(kernel, workload)
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -104,10 +110,236 @@ def cpu_model():
     return None
 
 
+def step_bytes(q, owned, valid, valid_cols, path, tile_codes=True):
+    """Algorithmic HBM bytes of one step of `path` over a shard of q slots
+    (owned tiles, valid elements, and valid_cols = the W^T rows of the owned
+    tiles), as (step kernel bytes, whole-step bytes incl. separate passes)."""
+    elems = q * 16384
+    grad = 4 * (elems if path == "unfused" else valid)
+    b = 24 * elems + grad
+    if tile_codes:
+        b += elems + 4 * q
+    if path in ("fused_unpack", "fused_unpack_t"):
+        b += valid + 4 * owned
+    if path == "fused_unpack_t":
+        b += valid + 4 * valid_cols
+    whole = b
+    if path in ("fused", "unfused"):
+        whole += owned * 16384 + valid + 8 * owned   # unpack_fp8
+    if path == "unfused":
+        whole += 4 * valid + 4 * elems                # pack_shard of the gradients
+    return b, whole
+
+
+def shard_counts(g):
+    owned = g.table[:g.owned]
+    return g.q, g.owned, int((owned[:, 4] * owned[:, 5]).sum()), int(owned[:, 5].sum())
+
+
+def timed(stream, fn, n):
+    """Mean ms of fn() over n calls, HIP events on `stream` around the run."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def setup(w, path="fused_unpack", pow2=False, layout="interleaved"):
+    """Device state of workload w, its prior steps taken, gradients of the
+    measured step drawn: ready for the timed steps."""
+    from bench_workload import GpuWorkload
+    transposed = path == "fused_unpack_t"
+    one_kernel = path in ("fused_unpack", "fused_unpack_t")
+    g = GpuWorkload(w, mode="fused_unpack" if one_kernel else path, pow2=pow2 or transposed,
+                    transposed=transposed, layout=layout)
+    g.tile_codes = True
+    g.load_state()
+    if w.steps[:-1]:
+        g.run_steps(w.steps[:-1])
+    g.draw_grads(w.measured_step)
+    return g
+
+
+def run_steps(g, path, steps, warmup, t_first, stream, fp8=None, sc=None):
+    """W untimed steps, then K timed ones; HIP events around the step
+    kernel, the fold and the unfold of every timed step."""
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    t = t_first
+
+    def one(t, e=None):
+        if path == "unfused":
+            e and e[2].record(stream)
+            g.pack_grads()
+            e and e[3].record(stream)
+        e and e[0].record(stream)
+        if path == "unfused":
+            g.step(t)
+        elif path == "fused":
+            g.fold_step(t)
+        else:
+            g.fold_step_unpack(t)
+        e and e[1].record(stream)
+        if path in ("fused", "unfused"):
+            e and e[4].record(stream)
+            g.unpack(fp8, sc)
+            e and e[5].record(stream)
+
+    for _ in range(warmup):
+        one(t)
+        t += 1
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for k in range(steps):
+        one(t, ev[k])
+        t += 1
+    end.record(stream)
+    torch.cuda.synchronize()
+    kms = [e[0].elapsed_time(e[1]) for e in ev]
+    res = {"ms_per_step": start.elapsed_time(end) / steps,
+           "kernel_ms": sum(kms) / steps,
+           "kernel_ms_min": min(kms) if kms else None,
+           "kernel_ms_max": max(kms) if kms else None,
+           "pack_ms": (sum(e[2].elapsed_time(e[3]) for e in ev) / steps
+                       if path == "unfused" else None),
+           "unpack_ms": (sum(e[4].elapsed_time(e[5]) for e in ev) / steps
+                         if path in ("fused", "unfused") else None),
+           "t_next": t}
+    return res
+
+
+def pass_stats(ms, algo, traffic=None):
+    gbps = algo / (ms * 1e-3) / 1e9
+    return {"ms": ms, "algorithmic_bytes": algo, "GBps": gbps, "frac": gbps / HBM_PEAK_GBPS,
+            "traffic": traffic}
+
+
+def time_pack_unpack(g, steps, stream):
+    """pack_shard of the row-major gradients into a tile-major buffer, and
+    unpack_fp8 of the step's codes and scales, each timed over `steps`
+    launches on the headline shard."""
+    import torch
+
+    import blockwise_fp8_zero_amd as bfz
+    q, owned, valid, _ = shard_counts(g)
+    g.grad = torch.empty(q * bfz.TILE_ELEMS, dtype=torch.float32, device=g.device)
+    g.pack_grads()
+    fp8, sc = (g.out_fp8, g.out_scale) if g.out_fp8 is not None else g.alloc_rowmajor_out()
+    g.unpack(fp8, sc)
+    torch.cuda.synchronize()
+    pack_ms = timed(stream, g.pack_grads, steps)
+    unpack_ms = timed(stream, lambda: g.unpack(fp8, sc), steps)
+    g.grad = None
+    torch.cuda.empty_cache()
+    return (pass_stats(pack_ms, 4 * valid + 4 * q * 16384),
+            pass_stats(unpack_ms, owned * 16384 + valid + 8 * owned))
+
+
+def time_transpose(g, t, steps, stream):
+    """One power-of-two step (so every tile scale is a power of two), then
+    bfz_transpose_pow2 of the shard timed over `steps` launches: W^T codes
+    and per-group power-of-two scales by exponent edits."""
+    import torch
+
+    import blockwise_fp8_zero_amd as bfz
+    pow2_was = g.pow2
+    g.pow2 = True
+    g.apply(t)
+    g.pow2 = pow2_was
+    dims = g.w.dims
+    dt = [None] * len(dims)
+    ds = [None] * len(dims)
+    for p in g.touched:
+        E, H, W = dims[p]
+        dt[p] = torch.empty(E * W * H, dtype=torch.uint8, device="cuda")
+        ds[p] = torch.empty(E * W * (-(-H // 128)), dtype=torch.float32, device="cuda")
+    bfz.transpose_pow2(g.plan, g.codes, g.scale_inv, dt, ds)
+    torch.cuda.synchronize()
+    ms = timed(stream, lambda: bfz.transpose_pow2(g.plan, g.codes, g.scale_inv, dt, ds), steps)
+    q, owned, valid, valid_cols = shard_counts(g)
+    # read: tile codes + scale; write: W^T codes of the valid elements + one
+    # scale per valid column of every owned tile
+    algo = q * bfz.TILE_ELEMS + 4 * q + valid + 4 * valid_cols
+    del dt, ds
+    torch.cuda.empty_cache()
+    out = pass_stats(ms, algo, measured_traffic("transpose_pow2_kernel", g.w.name))
+    out["kernel"] = "transpose_pow2_kernel"
+    return out
+
+
+def counter_reference_copy():
+    """A plain 1 GiB device copy (the runtime's copy kernel), once, outside
+    the timed region: the kernel of known size that rocprofv3's HBM byte
+    counters are scaled by."""
+    import torch
+    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    torch.cuda.empty_cache()
+
+
+def sampled_gpu_slots(g, n_random=24):
+    """The GPU's state, codes and scales of a sample of slots after the
+    measured step (first, last, weight boundaries, edges, zero tiles and a
+    seeded random draw), read back to the host for the oracle leg."""
+    from bench_workload import sample_slots
+    slots = sample_slots(g.w, g.table, g.q, g.owned, n_random=n_random)
+    return slots, g.tiles(slots)
+
+
+def oracle_leg(w, gpu_sample, tiny_gpu):
+    """The oracle's side of the run (the only part of bench.py that loads
+    it): parity counts of the sampled headline slots and of the tiny
+    workload, and the CPU baseline."""
+    import numpy as np
+
+    import oracle
+    from tests.compare import compare
+    from tests.oracle_run import oracle_slots
+
+    out = {}
+    slots, gpu = gpu_sample
+    ora = oracle_slots(w, slots)
+    rep = compare(gpu, ora)
+    out["headline"] = {"workload": w.name, "slots_compared": len(slots),
+                       "elements": len(slots) * oracle.TILE_ELEMS, "ok": rep["ok"],
+                       "bit_exact": rep["exact"], "code_mismatches": rep["codes_mismatch"],
+                       "midpoint_exceptions": rep["codes_mismatch_near_midpoint"],
+                       "near_midpoint_elems": rep["near_midpoint_elems"],
+                       "fp32_out_of_tolerance": rep["master_bad"] + rep["m_bad"] + rep["v_bad"],
+                       "scale_out_of_tolerance": rep["scale_bad"]}
+    tw, tg, tfp8 = tiny_gpu
+    tslots = list(range(len(tg["scale_inv"])))
+    tora = oracle_slots(tw, tslots)
+    trep = compare(tg, tora)
+    q, owned, table = oracle.plan(tw.dims, tw.D, tw.rank)
+    E, H, W = tw.dims[0]
+    o8 = np.zeros((E, H, W), dtype=np.uint8)
+    osc = np.zeros((E, -(-H // 128), -(-W // 128)), dtype=np.float32)
+    oracle.unpack(tw.dims, tora["codes"].reshape(-1), tora["scale_inv"], table, [o8], [osc])
+    unpack_exact = bool(np.array_equal(tfp8[0].reshape(-1), o8.reshape(-1))
+                        and np.array_equal(tfp8[1].reshape(-1), osc.reshape(-1)))
+    out["tiny"] = {"workload": tw.name, "slots_compared": len(tslots), "steps": len(tw.steps),
+                   "ok": trep["ok"], "bit_exact": trep["exact"],
+                   "code_mismatches": trep["codes_mismatch"],
+                   "midpoint_exceptions": trep["codes_mismatch_near_midpoint"],
+                   "row_major_unpack_exact": unpack_exact}
+    return out
+
+
 def cpu_baseline(w, target_s=10.0):
     """The C oracle (fold of the grads, AdamW + requant, unfold) on a slab of
-    the workload's first weight, 1024 x 4096 (256 tiles), stepped repeatedly
-    by every host thread for about target_s seconds."""
+    the workload's first weight, 1024 rows of it (8 tile rows), stepped
+    repeatedly by every host thread for about target_s seconds."""
     import ctypes as C
     from concurrent.futures import ThreadPoolExecutor
 
@@ -122,8 +354,10 @@ def cpu_baseline(w, target_s=10.0):
     dims = np.array([[E, H, W]], dtype=np.int64)
     q, owned, table = oracle.plan(dims, 1, 0)
     n = q * oracle.TILE_ELEMS
-    master_rm = synth.fill_rect_host(w.recipe(WL.MASTER, 0), 0, 0, H, 0, W)
-    grad_rm = synth.fill_rect_host(w.recipe(WL.GRAD, 0, w.measured_step), 0, 0, H, 0, W)
+    # the slab's own inputs: the workload's recipes for its first weight
+    rect = {k: synth.fill_rect_host(w.recipe(k, 0, w.measured_step), 0, 0, H, 0, W)
+            for k in (WL.MASTER, WL.GRAD, WL.MOM1, WL.MOM2)}
+    grad_rm = rect[WL.GRAD]
     L = oracle.lib()
     hp = oracle.hparams(step=w.measured_step, **WL.HP)
     P = C.c_void_p
@@ -142,11 +376,10 @@ def cpu_baseline(w, target_s=10.0):
         L.ora_unpack(ptr(dims), 1, ptr(codes), ptr(sc), ptr(table), q, C.cast(d8, P), C.cast(ds, P))
 
     def new_state():
-        srcs = [np.ascontiguousarray(master_rm.reshape(E, H, W))]
-        p = oracle.pack(dims, srcs, table)
-        return [np.empty(n, np.float32), p, np.zeros(n, np.float32), np.zeros(n, np.float32),
-                np.empty(n, np.uint8), np.empty(q, np.float32), np.empty(E * H * W, np.uint8),
-                np.empty(q, np.float32)]
+        fold = [oracle.pack(dims, [np.ascontiguousarray(rect[k].reshape(E, H, W))], table)
+                for k in (WL.MASTER, WL.MOM1, WL.MOM2)]
+        return [np.empty(n, np.float32), fold[0], fold[1], fold[2], np.empty(n, np.uint8),
+                np.empty(q, np.float32), np.empty(E * H * W, np.uint8), np.empty(q, np.float32)]
 
     # calibrate the number of passes on one thread (the second pass: the
     # first one takes the page faults of the fresh buffers)
@@ -157,13 +390,12 @@ def cpu_baseline(w, target_s=10.0):
     per_pass = time.perf_counter() - t0
     passes = max(1, int(round(target_s / per_pass)))
     # a one-thread figure over a 1 GiB tile subset (16384 tiles of master,
-    # the slab's state in 64 separate copies, so the data lives in DRAM, not
-    # in the caches), one pass over each copy
+    # the slab's state in separate copies, so the data lives in DRAM, not in
+    # the caches), one pass over each copy
     copies = [new_state() for _ in range(max(1, 16384 // q))]
     for c in copies:  # take the page faults of the fresh buffers now
-        for k, a in enumerate(c):
-            if k != 1:  # c[1] holds the folded master
-                a.fill(0)
+        for k in (0, 4, 5, 6, 7):
+            c[k].fill(0)
     t0 = time.perf_counter()
     for c in copies:
         one_pass(c)
@@ -189,51 +421,52 @@ def cpu_baseline(w, target_s=10.0):
             "one_thread_sample": f"one thread, one pass over {one_thread_gib:.2f} GiB of master "
                                  f"(the slab's state in {16384 // q} copies)",
             "nproc": os.cpu_count(), "cpu_model": cpu_model(),
-            "sample": f"fold + AdamW/E4M3 step + unfold of a {H}x{W} slab (256 tiles, "
-                      f"{n / 1e6:.1f}M elements) of the first dense-LLM weight at t="
-                      f"{w.measured_step}, {passes} passes on each of {threads} threads, "
-                      f"{dt:.1f} s wall",
+            "sample": f"fold + AdamW/E4M3 step + unfold of a {H}x{W} slab ({q} tiles, "
+                      f"{n / 1e6:.1f}M elements) of the first weight of the {w.name} workload, "
+                      f"its own master/m/v/grad draws, at t={w.measured_step}; {passes} passes "
+                      f"on each of {threads} threads, {dt:.1f} s wall",
             "seconds": round(dt, 2)}
 
 
-def time_transpose(g, t, steps, stream):
-    """One power-of-two step (so every tile scale is a power of two), then
-    bfz_transpose_pow2 of the shard timed over `steps` launches: W^T codes
-    and per-group power-of-two scales by exponent edits."""
-    import torch
+def tiny_gpu_run():
+    """The tiny workload (one 256x384 weight, 3 steps) through the same
+    one-kernel step and interleaved layout; results read back for the
+    oracle leg's parity counts."""
+    from bench_workload import GpuWorkload
+    from synth import workloads as WL
+    w = WL.tiny()
+    g = GpuWorkload(w, mode="fused_unpack", layout="interleaved")
+    g.load_state()
+    g.run_steps()
+    tiles = g.tiles(list(range(g.q)))
+    fp8, sc = g.rowmajor()
+    return w, tiles, (fp8[0].cpu().numpy(), sc[0].cpu().numpy())
 
-    import blockwise_fp8_zero_amd as bfz
-    pow2_was, tile_codes_was = g.pow2, g.tile_codes
-    g.pow2, g.tile_codes = True, True  # the transpose reads the tile-major codes
-    g.apply(t)
-    g.pow2, g.tile_codes = pow2_was, tile_codes_was
-    dims = g.w.dims
-    dt = [None] * len(dims)
-    ds = [None] * len(dims)
-    for p in g.touched:
-        E, H, W = dims[p]
-        dt[p] = torch.empty(E * W * H, dtype=torch.uint8, device="cuda")
-        ds[p] = torch.empty(E * W * (-(-H // 128)), dtype=torch.float32, device="cuda")
-    bfz.transpose_pow2(g.plan, g.codes, g.scale_inv, dt, ds)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        bfz.transpose_pow2(g.plan, g.codes, g.scale_inv, dt, ds)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    owned = g.table[:g.owned]
-    valid = int((owned[:, 4] * owned[:, 5]).sum())
-    # read: tile codes + scale; write: W^T codes of the valid elements + one
-    # scale per valid column of every owned tile
-    algo = g.q * bfz.TILE_ELEMS + 4 * g.q + valid + 4 * int(owned[:, 5].sum())
-    del dt, ds
-    traffic = measured_traffic("transpose_pow2_kernel") if g.w.name == "dense_llm" else None
-    return {"kernel": "transpose_pow2_kernel", "ms": ms, "algorithmic_bytes": algo,
-            "GBps": algo / (ms * 1e-3) / 1e9, "frac": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-            "traffic": traffic}
+
+def config_line(w, args, stream):
+    """One of the other shard workloads through the default one-kernel step,
+    timed like the headline (its own set-up, W + K steps)."""
+    import torch
+    t0 = time.perf_counter()
+    g = setup(w)
+    r = run_steps(g, "fused_unpack", args.steps, args.warmup, w.measured_step, stream)
+    q, owned, valid, valid_cols = shard_counts(g)
+    algo, _ = step_bytes(q, owned, valid, valid_cols, "fused_unpack")
+    elems = q * 16384
+    out = {"workload": f"{w.name}: {w.description}", "shard_tiles": q, "shard_elems": elems,
+           "valid_elems": valid, "D": w.D, "rank": w.rank, "ms_per_step": r["ms_per_step"],
+           "value": elems / (r["ms_per_step"] * 1e-3),
+           "valid_elems_per_s": valid / (r["ms_per_step"] * 1e-3),
+           "step_kernel_ms": r["kernel_ms"],
+           "step_kernel_ms_min_max": [r["kernel_ms_min"], r["kernel_ms_max"]],
+           "algorithmic_bytes_per_step": algo,
+           "roofline_frac": algo / (r["kernel_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+           "traffic": measured_traffic("fold_step_unfold_kernel", w.name)}
+    del g
+    torch.cuda.empty_cache()
+    log(f"config {w.name}: {r['ms_per_step']:.4f} ms/step, frac {out['roofline_frac']:.4f} "
+        f"({time.perf_counter() - t0:.1f} s)")
+    return out
 
 
 def main():
@@ -241,15 +474,18 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dense_llm",
-                    choices=["dense_llm", "ragged", "moe_experts", "large", "tiny"])
-    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="large",
+                    choices=["large", "dense_llm", "ragged", "moe_experts", "tiny"])
+    ap.add_argument("--skip-cpu-baseline", action="store_true",
+                    help="skip the oracle leg (CPU baseline and parity counts)")
+    ap.add_argument("--skip-configs", action="store_true",
+                    help="do not time the other shard workloads after the headline")
+    ap.add_argument("--skip-passes", action="store_true",
+                    help="do not time pack / unpack / transpose / copy after the steps")
     ap.add_argument("--path", default="fused_unpack", choices=list(KERNEL_OF_PATH),
                     help="which entry points make up a step (see the module docstring)")
     ap.add_argument("--pow2", action="store_true",
-                    help="power-of-two tile scales in the timed steps (bfz_adamw.scale_pow2)")
-    ap.add_argument("--skip-transpose", action="store_true",
-                    help="do not time bfz_transpose_pow2 after the steps")
+                    help="power-of-two tile scales in the timed steps")
     ap.add_argument("--layout", default="interleaved", choices=["interleaved", "separate"],
                     help="FP32 state layout (see the module docstring)")
     args = ap.parse_args()
@@ -261,131 +497,39 @@ def main():
     import torch
 
     import blockwise_fp8_zero_amd as bfz
+    from bench_workload import launch_segments
     from synth import workloads as WL
-    from bench_workload import GpuWorkload
 
     torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
     w = WL.BY_NAME[args.workload]()
     log(f"workload {w.name}: {w.description}")
     t0 = time.perf_counter()
-    # fused_unpack_t: the one-kernel step with power-of-two scales that also
-    # writes the transposed copy W^T
-    transposed = args.path == "fused_unpack_t"
+    g = setup(w, args.path, args.pow2, args.layout)
     one_kernel = args.path in ("fused_unpack", "fused_unpack_t")
-    g = GpuWorkload(w, mode="fused_unpack" if one_kernel else args.path,
-                    pow2=args.pow2 or transposed, transposed=transposed, layout=args.layout)
-    # a lone rank (D = 1) gathers nothing: its one-kernel step writes only
-    # the row-major FP8 weights and scale grids, not the tile-major copy
-    lone = one_kernel and w.D == 1
-    g.load_state()
-    prior = w.steps[:-1]
-    if prior:
-        g.run_steps(prior)
-    g.draw_grads(w.measured_step)
     fp8, sc = g.alloc_rowmajor_out() if not one_kernel else (None, None)
-    # a plain 1 GiB device copy, outside the timed region: the reference
-    # kernel of known size for scaling the HBM byte counters
-    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
-    b = torch.empty_like(a)
-    b.copy_(a)
-    del a, b
-    torch.cuda.synchronize()
+    # the measured step itself, once, from the seeded state: a sample of its
+    # slots goes to the oracle leg for the parity counts
+    first = run_steps(g, args.path, 1, 0, w.measured_step, stream, fp8, sc)
+    gpu_sample = None if args.skip_cpu_baseline else sampled_gpu_slots(g)
+    counter_reference_copy()
     log(f"set-up {time.perf_counter() - t0:.1f} s; q={g.q} tiles, owned={g.owned}")
 
-    stream = torch.cuda.current_stream()
-    t_next = w.measured_step
-
-    def one_step(t, ev=None):
-        # ev: HIP events around the step kernel (0, 1), the fold (2, 3) and
-        # the unfold (4, 5), recorded on the stream the kernels run on
-        if args.path == "unfused":
-            if ev is not None:
-                ev[2].record(stream)
-            g.pack_grads()
-            if ev is not None:
-                ev[3].record(stream)
-        if ev is not None:
-            ev[0].record(stream)
-        if args.path == "unfused":
-            g.step(t)
-        elif args.path == "fused":
-            g.fold_step(t)
-        else:
-            g.fold_step_unpack(t)
-        if ev is not None:
-            ev[1].record(stream)
-        if not one_kernel:
-            if ev is not None:
-                ev[4].record(stream)
-            g.unpack(fp8, sc)
-            if ev is not None:
-                ev[5].record(stream)
-
-    g.tile_codes = not lone
-    for _ in range(args.warmup):
-        one_step(t_next)
-        t_next += 1
-    torch.cuda.synchronize()
-
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(6)) for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for k in range(args.steps):
-        one_step(t_next, evs[k])
-        t_next += 1
-    end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    step_kernel_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    pack_ms = (sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
-               if args.path == "unfused" else None)
-    unpack_ms = (sum(e[4].elapsed_time(e[5]) for e in evs) / args.steps
-                 if not one_kernel else None)
-    ms_per_step = total_ms / args.steps
-
-    elems = g.q * bfz.TILE_ELEMS
-    valid = int((g.table[:g.owned, 4] * g.table[:g.owned, 5]).sum())
+    r = run_steps(g, args.path, args.steps, args.warmup, first["t_next"], stream, fp8, sc)
+    q, owned, valid, valid_cols = shard_counts(g)
     kernel = KERNEL_OF_PATH[args.path]
-    # fused kernels read the gradient of valid elements only
-    grad_elems = elems if args.path == "unfused" else valid
-    # master, m, v read and written (24 B), the gradient read (4 B, valid
-    # elements only when read row-major), the tile-major code and scale
-    algo_bytes = (STEP_BYTES_PER_ELEM - 5) * elems + 4 * grad_elems
-    if not lone:
-        algo_bytes += elems + STEP_BYTES_PER_TILE * g.q
-    if one_kernel:
-        # row-major codes of the valid elements and the scale-grid cells
-        algo_bytes += valid + 4 * g.owned
-    if transposed:
-        # W^T codes of the valid elements, one scale per W^T row group
-        algo_bytes += valid + 4 * int(g.table[:g.owned, 5].sum())
-    achieved = algo_bytes / (step_kernel_ms * 1e-3) / 1e9
-    whole_bytes = algo_bytes
-    if not one_kernel:
-        whole_bytes += UNPACK_BYTES_PER_ELEM * elems + UNPACK_BYTES_PER_TILE * g.q
-    if args.path == "unfused":
-        whole_bytes += PACK_BYTES_PER_ELEM * elems
-    traffic = measured_traffic(kernel) if w.name == "dense_llm" and kernel in TRAFFIC_FILES else None
-    transpose = None
-    if not args.skip_transpose:
-        transpose = time_transpose(g, t_next, args.steps, stream)
-
-    def pass_stats(ms, algo):
-        if ms is None:
-            return None
-        gbps = algo / (ms * 1e-3) / 1e9
-        return {"ms": ms, "algorithmic_bytes": algo, "GBps": gbps, "frac": gbps / HBM_PEAK_GBPS}
+    algo, whole = step_bytes(q, owned, valid, valid_cols, args.path)
+    elems = q * bfz.TILE_ELEMS
+    achieved = algo / (r["kernel_ms"] * 1e-3) / 1e9
 
     out = {
         "metric": METRIC,
-        "value": elems / (ms_per_step * 1e-3),
+        "value": elems / (r["ms_per_step"] * 1e-3),
         "unit": "elem/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -393,12 +537,14 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: {w.description}",
-            "shard_tiles": g.q,
+            "shard_tiles": q,
             "shard_elems": elems,
             "valid_elems": valid,
+            "value_counts": "shard elements incl. padding slots and edge padding "
+                            "(valid_elems_per_s counts the weights' own elements)",
             "D": w.D,
             "rank": w.rank,
-            "first_timed_step_t": w.measured_step + args.warmup,
+            "first_timed_step_t": first["t_next"] + args.warmup,
             "state_layout": {"interleaved": "one [master | m | v] block per tile "
                                             "(state_stride 49152)",
                              "separate": "three tile-major arrays"}[args.layout],
@@ -406,14 +552,16 @@ def main():
                           "fused": "fold_adamw_fp8_step + unpack_fp8",
                           "fused_unpack": "fold_adamw_fp8_step_unpack",
                           "fused_unpack_t": "fold_adamw_fp8_step_unpack_t (power-of-two scales, "
-                                            "plus the transposed copy W^T)"}[args.path]
-                         + (" (row-major output only: D = 1)" if lone else ""),
+                                            "plus the transposed copy W^T)"}[args.path],
+            "outputs": "tile-major codes + scale_inv (the all-gather payload) and row-major "
+                       "FP8 weights + scale grids",
         },
-        "valid_elems_per_s": valid / (ms_per_step * 1e-3),
-        "step_hbm_GBps": whole_bytes / (ms_per_step * 1e-3) / 1e9,
-        "step_hbm_frac": whole_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "step_kernel_ms": step_kernel_ms,
-        "step_kernel_elems_per_s": elems / (step_kernel_ms * 1e-3),
+        "valid_elems_per_s": valid / (r["ms_per_step"] * 1e-3),
+        "step_hbm_GBps": whole / (r["ms_per_step"] * 1e-3) / 1e9,
+        "step_hbm_frac": whole / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "step_kernel_ms": r["kernel_ms"],
+        "step_kernel_ms_min_max": [r["kernel_ms_min"], r["kernel_ms_max"]],
+        "step_kernel_elems_per_s": elems / (r["kernel_ms"] * 1e-3),
         "roofline": {
             "kernel": kernel,
             "bound": "hbm",
@@ -421,20 +569,36 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": algo_bytes,
+            "traffic": measured_traffic(kernel, w.name),
+            "algorithmic_bytes_per_launch": algo,
+            "launches_per_step": launch_segments(g.table, owned, q),
         },
         "cpu_baseline": None,
-        "transpose_pow2": transpose,
-        # the fold and the unfold as passes of their own (unfused / fused
-        # routes): fold reads the valid gradient elements and writes whole
-        # tiles; unfold reads the owned tiles' codes and scales and writes
-        # the valid codes and the scale-grid cells
-        "pack": pass_stats(pack_ms, 4 * valid + 4 * elems),
-        "unpack": pass_stats(unpack_ms, g.owned * bfz.TILE_ELEMS + valid + 8 * g.owned),
+        "parity": None,
+        "pack": None,
+        "unpack": None,
+        "transpose_pow2": None,
+        "configs": None,
     }
+    if r["pack_ms"] is not None:
+        out["pack"] = pass_stats(r["pack_ms"], 4 * valid + 4 * elems)
+    if r["unpack_ms"] is not None:
+        out["unpack"] = pass_stats(r["unpack_ms"], owned * 16384 + valid + 8 * owned)
+    if not args.skip_passes:
+        if out["pack"] is None or out["unpack"] is None:
+            p_, u_ = time_pack_unpack(g, args.steps, stream)
+            out["pack"] = out["pack"] or p_
+            out["unpack"] = out["unpack"] or u_
+        out["transpose_pow2"] = time_transpose(g, r["t_next"], args.steps, stream)
+    del g
+    torch.cuda.empty_cache()
+    if not args.skip_configs:
+        out["configs"] = {n: config_line(WL.BY_NAME[n](), args, stream)
+                          for n in OTHER_CONFIGS if n != w.name}
     if not args.skip_cpu_baseline:
-        log("cpu baseline (oracle) ...")
+        tiny = tiny_gpu_run()
+        log("oracle leg: parity counts and cpu baseline ...")
+        out["parity"] = oracle_leg(w, gpu_sample, tiny)
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
 

@@ -187,3 +187,44 @@ class GpuWorkload:
 
         return dict(master=take(self.master), m=take(self.m), v=take(self.v),
                     codes=take(self.codes), scale_inv=self.scale_inv[idx].cpu().numpy())
+
+
+def sample_slots(w, table, q, owned, n_random=24, seed=0):
+    """A sample of a shard's slots for spot checks: first, last owned and
+    last, the two slots at each weight boundary (up to 60), the first and
+    last 8 edge slots, up to 8 all-zero tiles where the workload has them,
+    and n_random seeded random slots.  table: the plan's [q, 6] table."""
+    pick = {0, max(0, owned - 1), q - 1}
+    for s in range(1, owned):
+        if table[s][0] != table[s - 1][0]:
+            pick.update((s - 1, s))
+        if len(pick) > 60:
+            break
+    edge = [s for s in range(owned) if table[s][4] < 128 or table[s][5] < 128]
+    pick.update(edge[:8] + edge[-8:])
+    if w.zero_tile_prob > 0:
+        zeros = []
+        for s in range(owned):
+            p, e, i, j = (int(x) for x in table[s][:4])
+            E, H, W = w.dims[p]
+            hb, wb = -(-H // 128), -(-W // 128)
+            if synth.lib().synth_uniform(w._zero_key(p), (e * hb + i) * wb + j) < w.zero_tile_prob:
+                zeros.append(s)
+            if len(zeros) >= 8:
+                break
+        pick.update(zeros)
+    rng = np.random.default_rng(seed)
+    pick.update(int(x) for x in rng.integers(0, q, size=min(n_random, q)))
+    return sorted(pick)
+
+
+def launch_segments(table, owned, q, per_launch=64):
+    """Launches one call of a plan-driven entry point makes: runs of owned
+    slots whose weights span fewer than per_launch weight indices, plus one
+    for the padding slots."""
+    n, first = 0, None
+    for s in range(owned):
+        p = int(table[s][0])
+        if first is None or p - first >= per_launch:
+            n, first = n + 1, p
+    return n + (1 if owned < q else 0)

@@ -87,7 +87,6 @@ __device__ __forceinline__ void adamw_elem(float& p, float g, float& m, float& v
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 load_stream(const f32x4* p) { return __builtin_nontemporal_load(p); }
-__device__ __forceinline__ void store_stream(f32x4* p, f32x4 v) { __builtin_nontemporal_store(v, p); }
 __device__ __forceinline__ void store_stream(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
 
 // A tile's blocks in the shard arrays (master, m, v, a tile-major gradient:
@@ -131,30 +130,34 @@ __device__ __forceinline__ uint32_t pack_codes(const f32x4& x, float scale) {
 }
 
 // Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD
-// b % 8).  Map them so each XCD walks one contiguous eighth of the tiles:
-// the XCDs then stream from 8 compact address windows instead of all of
-// them interleaving tile by tile.  Bijective for any n_tiles.
-__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t n_tiles) {
-    const int64_t per = n_tiles / 8, x = b % 8, j = b / 8;
-    return j < per ? x * per + j : 8 * per + x;
-}
-
-// The step kernels' order: runs of kStepRun consecutive tiles per XCD,
-// dealt round-robin, so the workgroups in flight cover one compact window
-// of consecutive tiles (dispatch order) while each XCD's L2 still sees
-// neighbouring tiles -- whose row-major gradient rows and code rows share
-// DRAM pages -- back to back.  Workgroup b = 8 j + x (XCD x) takes tile
-// 8 R (j / R) + R x + j % R; the last n % (8 R) tiles keep their own index.
-// Bijective for any n_tiles.  Measured against the XCD-contiguous order
-// (xcd_tile), one-kernel step, same process: 2.01B-element shard 9.75 ->
-// 9.58 ms, dense 3.92 -> 3.88, MoE 1.71 -> 1.69, ragged 0.366 -> 0.359
-// (runs of 2 within 0.5% of 4; 8 and 16 slower; plain order in between).
-constexpr int64_t kStepRun = 4;
-__device__ __forceinline__ int64_t step_tile_of(int64_t b, int64_t n_tiles) {
-    const int64_t full = n_tiles / (8 * kStepRun) * (8 * kStepRun);
+// b % 8).  The streaming kernels map them to tiles in runs of R consecutive
+// tiles per XCD, dealt round-robin: workgroup b = 8 j + x (XCD x) takes tile
+// 8 R (j / R) + R x + j % R, and the last n % (8 R) tiles keep their own
+// index.  The workgroups in flight then cover one compact window of
+// consecutive tiles (dispatch order), while each XCD's L2 sees R
+// neighbouring tiles -- whose row-major rows share DRAM pages -- back to
+// back.  Bijective for any n_tiles.  R per kernel, measured on MI355X
+// against one contiguous eighth of the shard per XCD (the earlier order),
+// each A/B in one process on one box:
+//   step kernels, R = 4: one-kernel step 2.01B-element shard 9.75 -> 9.58 ms,
+//     dense 3.92 -> 3.88, MoE 1.71 -> 1.69, ragged 0.366 -> 0.359 (R = 2
+//     within 0.5% of 4; 8 and 16 slower);
+//   fold (pack_kernel), R = 2: dense 1.034 -> 1.023 ms, 2.01B 2.527 -> 2.477,
+//     ragged unchanged (longer runs up to 2% slower on the large shards);
+//   unfold (unpack_kernel), R = 32 (a whole tile row of a 4096-wide weight
+//     per XCD): dense 0.280 -> 0.268 ms, 2.01B 0.688 -> 0.657, ragged
+//     0.0468 -> 0.0451 (R = 2..16 in between, 64 slightly slower).
+// The transpose keeps plain order (below).
+template <int64_t R>
+__device__ __forceinline__ int64_t run_tile(int64_t b, int64_t n_tiles) {
+    const int64_t full = n_tiles / (8 * R) * (8 * R);
     if (b >= full) return b;
     const int64_t x = b % 8, j = b / 8;
-    return (j / kStepRun) * (8 * kStepRun) + x * kStepRun + j % kStepRun;
+    return (j / R) * (8 * R) + x * R + j % R;
+}
+constexpr int64_t kStepRun = 4, kPackRun = 2, kUnpackRun = 32;
+__device__ __forceinline__ int64_t step_tile_of(int64_t b, int64_t n_tiles) {
+    return run_tile<kStepRun>(b, n_tiles);
 }
 
 // One 1024-thread workgroup (16 wave64s) owns one tile: each thread holds
@@ -470,7 +473,7 @@ __global__ __launch_bounds__(kStepThreads) void fold_step_unfold_kernel(
 __global__ __launch_bounds__(kStepThreads) void pack_kernel(const TileEntry* __restrict__ entries,
                                                             float* __restrict__ dst, int64_t dst_stride,
                                                             PackArgs args) {
-    const int64_t slot = xcd_tile(blockIdx.x, gridDim.x);
+    const int64_t slot = run_tile<kPackRun>(blockIdx.x, gridDim.x);
     const TileEntry t = entries[slot];
     f32x4* out = reinterpret_cast<f32x4*>(dst + slot * dst_stride);
     const TileBlock block(out, kTileElems * 4);
@@ -487,8 +490,9 @@ __global__ __launch_bounds__(kStepThreads) void pack_kernel(const TileEntry* __r
     });
 }
 
-// Unfold of codes and scales: one workgroup per owned slot, XCD-contiguous
-// (measured 5.6% faster than plain order on the dense shard).  Thread t moves
+// Unfold of codes and scales: one workgroup per owned slot, in runs of 32
+// tiles per XCD (run_tile; plain order measured 5.6% slower on the dense
+// shard than one contiguous eighth per XCD, itself 4% slower than this).  Thread t moves
 // 16 codes (column block t % 8) of rows t / 8, t / 8 + 32, ...  A row of a
 // full-width tile goes out as one 16-byte store per lane when it starts on a
 // 16-byte boundary, as 4-byte words when on a 4-byte boundary, and otherwise
@@ -503,7 +507,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const TileEntry* __res
                                                           const float* __restrict__ scale_inv,
                                                           UnpackArgs args) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const int64_t slot = xcd_tile(blockIdx.x, gridDim.x);
+    const int64_t slot = run_tile<kUnpackRun>(blockIdx.x, gridDim.x);
     const TileEntry t = entries[slot];
     if (t.local < 0) return;
     const u32x4* in = reinterpret_cast<const u32x4*>(codes + slot * kTileElems);
@@ -740,9 +744,10 @@ __global__ __launch_bounds__(kThreads) void transpose_pow2_kernel(
     const float* __restrict__ scale_inv, TransposeArgs args) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     __shared__ uint32_t tile_t[kTileDim * 32];
-    // Plain order (workgroup b on XCD b % 8), measured 1.5-7% faster here
-    // than XCD-contiguous ranges (likely because each XCD's tiles in flight
-    // then span more tile rows of the same tile columns: longer W^T row runs).
+    // Plain order (workgroup b on XCD b % 8): measured 1.5-7% faster here
+    // than one contiguous eighth of the shard per XCD, and 1-7% faster than
+    // runs of 2 to 8 consecutive tiles per XCD (run_tile), on the dense and
+    // 2.01B-element shards.
     const int64_t slot = blockIdx.x;
     const TileEntry t = entries[slot];
     if (t.local < 0) return;

@@ -26,16 +26,34 @@ def test_timed_path_does_not_load_the_oracle():
 
 
 def test_traffic_is_reported_only_for_the_profiled_kernel_source(tmp_path, monkeypatch):
-    good = tmp_path / "good.md"
-    stale = tmp_path / "stale.md"
+    good = tmp_path / "step_kernel_good_traffic.md"
+    stale = tmp_path / "step_kernel_stale_traffic.md"
     good.write_text(f"kernel_sha256: {bench.kernel_sha()}\ntraffic_bytes_per_launch: 2.5e+10\n")
     stale.write_text("kernel_sha256: " + "0" * 64 + "\ntraffic_bytes_per_launch: 2.5e+10\n")
-    monkeypatch.setitem(bench.TRAFFIC_FILES, "step_kernel", str(good))
-    assert bench.measured_traffic("step_kernel") == 2.5e10
-    monkeypatch.setitem(bench.TRAFFIC_FILES, "step_kernel", str(stale))
-    assert bench.measured_traffic("step_kernel") is None
-    monkeypatch.setitem(bench.TRAFFIC_FILES, "step_kernel", str(tmp_path / "missing.md"))
-    assert bench.measured_traffic("step_kernel") is None
+    monkeypatch.setattr(bench, "traffic_file",
+                        lambda kernel, workload: str(tmp_path / f"{kernel}_{workload}_traffic.md"))
+    assert bench.measured_traffic("step_kernel", "good") == 2.5e10
+    assert bench.measured_traffic("step_kernel", "stale") is None
+    assert bench.measured_traffic("step_kernel", "missing") is None
+
+
+def test_step_bytes_accounting():
+    """The one-kernel step's algorithmic bytes: 30 B per element + 8 B per
+    tile on full tiles (24 B of state, 4 B of gradient, the tile-major and the
+    row-major code, scale_inv and the scale-grid cell); the fused route moves
+    the unfold into a pass of its own, the unfused one the fold as well."""
+    q, owned = 10, 9
+    valid = 9 * 16384 - 100
+    one, whole = bench.step_bytes(q, owned, valid, 9 * 128, "fused_unpack")
+    assert one == whole == 24 * q * 16384 + 4 * valid + q * 16384 + 4 * q + valid + 4 * owned
+    full, _ = bench.step_bytes(5, 5, 5 * 16384, 5 * 128, "fused_unpack")
+    assert full == 30 * 5 * 16384 + 8 * 5
+    step, whole = bench.step_bytes(q, owned, valid, 0, "fused")
+    assert step == 24 * q * 16384 + 4 * valid + q * 16384 + 4 * q
+    assert whole == step + owned * 16384 + valid + 8 * owned
+    step, whole = bench.step_bytes(q, owned, valid, 0, "unfused")
+    assert step == 29 * q * 16384 + 4 * q
+    assert whole == step + owned * 16384 + valid + 8 * owned + 4 * valid + 4 * q * 16384
 
 
 def test_kernel_hash_follows_code_not_comments(tmp_path, monkeypatch):

@@ -138,6 +138,55 @@ def test_full_size_sampled(name, mode):
     _free()
 
 
+def test_moe_full_size_every_slot():
+    """The MoE expert shard (D = 32, rank 0: 21,504 tiles, 352M elements) at
+    full size, in the launch configuration and state layout bench.py times,
+    compared with the oracle on every slot -- master, m, v, tile-major codes
+    and scale_inv, and the row-major FP8 weights and scale grid of every
+    owned tile against the oracle's own unfold.  Compared in chunks of 2048
+    slots so host memory stays bounded; midpoint cases are counted."""
+    w = WL.moe()
+    _say("moe_experts full size, every slot, mode fused_unpack, layout", BENCH_LAYOUT, "seed",
+         w.seed)
+    g = GpuWorkload(w, mode="fused_unpack", layout=BENCH_LAYOUT)
+    g.load_state()
+    g.run_steps()
+    q, owned, table = oracle.plan(w.dims, w.D, w.rank)
+    assert q == g.q == 21504 and owned == q
+    ora_codes = np.empty((q, 16384), dtype=np.uint8)
+    ora_scale = np.empty(q, dtype=np.float32)
+    totals = {"codes_mismatch": 0, "codes_mismatch_near_midpoint": 0, "near_midpoint_elems": 0}
+    exact = True
+    chunk = 2048
+    for s0 in range(0, q, chunk):
+        slots = list(range(s0, min(q, s0 + chunk)))
+        ora = oracle_slots(w, slots)
+        rep = compare(g.tiles(slots), ora)
+        assert rep["ok"], (s0, rep["fail"])
+        exact &= rep["exact"]
+        for k in totals:
+            totals[k] += rep[k]
+        ora_codes[s0:s0 + len(slots)] = ora["codes"]
+        ora_scale[s0:s0 + len(slots)] = ora["scale_inv"]
+        _say(f"moe slots {s0}..{s0 + len(slots) - 1}: exact={rep['exact']}")
+        del ora
+    _say("moe every slot:", q, "slots, bit-exact", exact, totals)
+    assert exact
+    # row-major output of the owned tiles (gate of experts 0..23): the
+    # oracle's unfold of its own codes
+    experts = int(table[owned - 1][1]) + 1
+    E, H, W = w.dims[0]
+    o8 = np.zeros((experts, H, W), dtype=np.uint8)
+    osc = np.zeros((experts, -(-H // 128), -(-W // 128)), dtype=np.float32)
+    oracle.unpack([(experts, H, W)], ora_codes.reshape(-1), ora_scale, table, [o8], [osc])
+    fp8, sc = g.rowmajor()
+    torch.cuda.synchronize()
+    assert np.array_equal(fp8[0][:experts * H * W].cpu().numpy(), o8.reshape(-1))
+    assert np.array_equal(sc[0][:osc.size].cpu().numpy(), osc.reshape(-1))
+    del g
+    _free()
+
+
 def test_lone_rank_rowmajor_only_full_size():
     """The 2.01B-element workload (D = 1) as the bench steps it: the
     one-kernel step with no tile-major codes or scales, only the row-major
