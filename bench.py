@@ -31,8 +31,12 @@ roofline = the step kernel's algorithmic HBM bytes per step (master, m, v
 read and written: 24 B per element; the gradient read: 4 B per valid
 element; the tile-major code: 1 B per element; scale_inv: 4 B per tile; the
 row-major code: 1 B per valid element; the scale-grid cell: 4 B per owned
-tile) over its mean launch time, measured with HIP events on the stream the
-kernels run on.  After the timed region, outside it:
+tile) over its mean time per step, measured with HIP events on the stream
+the kernels run on.  A step is one launch per segment of at most 64
+weights (two on the headline shard, same rate per tile), so bytes per step
+over time per step equals bytes per launch over launch time; traffic =
+the committed rocprofv3 FETCH_SIZE + WRITE_SIZE bytes per step of the same
+kernel, while the kernel source still hashes as when they were taken.  After the timed region, outside it:
   configs: the other shard workloads (dense-LLM, MoE experts, ragged)
       through the same one-kernel step, each timed the same way;
   pack / unpack: pack_shard of the gradients and unpack_fp8 of the codes
@@ -85,15 +89,15 @@ def kernel_sha():
 
 
 def measured_traffic(kernel, workload):
-    """HBM bytes per launch set of `kernel` on `workload` from its committed
-    rocprofv3 PMC summary, if that was taken on the current kernel source;
-    else None."""
+    """HBM bytes of `kernel` per call of its entry point (all launch segments
+    of one step or pass) on `workload`, from its committed rocprofv3 PMC
+    summary, if that was taken on the current kernel source; else None."""
     path = traffic_file(kernel, workload)
     if not os.path.exists(path):
         return None
     text = open(path).read()
     sha = re.search(r"kernel_sha256:\s*([0-9a-f]{64})", text)
-    tb = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    tb = re.search(r"traffic_bytes_per_call:\s*([0-9.eE+]+)", text)
     if not sha or not tb or sha.group(1) != kernel_sha():
         return None
     return float(tb.group(1))
@@ -238,8 +242,9 @@ def time_pack_unpack(g, steps, stream):
     unpack_ms = timed(stream, lambda: g.unpack(fp8, sc), steps)
     g.grad = None
     torch.cuda.empty_cache()
-    return (pass_stats(pack_ms, 4 * valid + 4 * q * 16384),
-            pass_stats(unpack_ms, owned * 16384 + valid + 8 * owned))
+    return (pass_stats(pack_ms, 4 * valid + 4 * q * 16384, measured_traffic("pack_kernel", g.w.name)),
+            pass_stats(unpack_ms, owned * 16384 + valid + 8 * owned,
+                       measured_traffic("unpack_kernel", g.w.name)))
 
 
 def time_transpose(g, t, steps, stream):
@@ -570,7 +575,7 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": measured_traffic(kernel, w.name),
-            "algorithmic_bytes_per_launch": algo,
+            "algorithmic_bytes_per_step": algo,
             "launches_per_step": launch_segments(g.table, owned, q),
         },
         "cpu_baseline": None,

@@ -28,8 +28,8 @@ def test_timed_path_does_not_load_the_oracle():
 def test_traffic_is_reported_only_for_the_profiled_kernel_source(tmp_path, monkeypatch):
     good = tmp_path / "step_kernel_good_traffic.md"
     stale = tmp_path / "step_kernel_stale_traffic.md"
-    good.write_text(f"kernel_sha256: {bench.kernel_sha()}\ntraffic_bytes_per_launch: 2.5e+10\n")
-    stale.write_text("kernel_sha256: " + "0" * 64 + "\ntraffic_bytes_per_launch: 2.5e+10\n")
+    good.write_text(f"kernel_sha256: {bench.kernel_sha()}\ntraffic_bytes_per_call: 2.5e+10\n")
+    stale.write_text("kernel_sha256: " + "0" * 64 + "\ntraffic_bytes_per_call: 2.5e+10\n")
     monkeypatch.setattr(bench, "traffic_file",
                         lambda kernel, workload: str(tmp_path / f"{kernel}_{workload}_traffic.md"))
     assert bench.measured_traffic("step_kernel", "good") == 2.5e10
