@@ -48,6 +48,7 @@ kernel, while the kernel source still hashes as when they were taken.  After the
       headline workload, on the host's cores.
 """
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -140,16 +141,35 @@ def shard_counts(g):
     return g.q, g.owned, int((owned[:, 4] * owned[:, 5]).sum()), int(owned[:, 5].sum())
 
 
+class no_gc:
+    """Python's garbage collector held off from before the warm-up until the
+    timed loop is done: a collection pause on the host while the device
+    queue runs dry would be timed as device time, and one between warm-up
+    and timing would let the device idle (and its clocks drop) before the
+    first timed step.  The collection runs first, before any warm-up."""
+
+    def __enter__(self):
+        gc.collect()
+        gc.disable()
+
+    def __exit__(self, *exc):
+        gc.enable()
+
+
 def timed(stream, fn, n):
-    """Mean ms of fn() over n calls, HIP events on `stream` around the run."""
+    """Mean ms of fn() over n calls, HIP events on `stream` around the run,
+    after one untimed call."""
     import torch
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(n):
+    with no_gc():
         fn()
-    e1.record(stream)
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
     return e0.elapsed_time(e1) / n
 
 
@@ -194,18 +214,19 @@ def run_steps(g, path, steps, warmup, t_first, stream, fp8=None, sc=None):
             g.unpack(fp8, sc)
             e and e[5].record(stream)
 
-    for _ in range(warmup):
-        one(t)
-        t += 1
-    torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for k in range(steps):
-        one(t, ev[k])
-        t += 1
-    end.record(stream)
-    torch.cuda.synchronize()
+    with no_gc():
+        for _ in range(warmup):
+            one(t)
+            t += 1
+        torch.cuda.synchronize()
+        start.record(stream)
+        for k in range(steps):
+            one(t, ev[k])
+            t += 1
+        end.record(stream)
+        torch.cuda.synchronize()
     kms = [e[0].elapsed_time(e[1]) for e in ev]
     res = {"ms_per_step": start.elapsed_time(end) / steps,
            "kernel_ms": sum(kms) / steps,
@@ -289,7 +310,6 @@ def counter_reference_copy():
     b.copy_(a)
     torch.cuda.synchronize()
     del a, b
-    torch.cuda.empty_cache()
 
 
 def sampled_gpu_slots(g, n_random=24):
@@ -450,16 +470,22 @@ def tiny_gpu_run():
 
 def config_line(w, args, stream):
     """One of the other shard workloads through the default one-kernel step,
-    timed like the headline (its own set-up, W + K steps)."""
+    timed like the headline (its own set-up, warm-up and timed steps); a
+    short shard takes more steps than K, enough for about 50 ms of timed
+    work at the headline's rate, so one host or device hiccup weighs less."""
     import torch
     t0 = time.perf_counter()
     g = setup(w)
-    r = run_steps(g, "fused_unpack", args.steps, args.warmup, w.measured_step, stream)
     q, owned, valid, valid_cols = shard_counts(g)
     algo, _ = step_bytes(q, owned, valid, valid_cols, "fused_unpack")
+    est_ms = algo / 6.3e12 * 1e3
+    steps = max(args.steps, int(50.0 / est_ms))
+    warmup = max(args.warmup, steps // 4)
+    r = run_steps(g, "fused_unpack", steps, warmup, w.measured_step, stream)
     elems = q * 16384
     out = {"workload": f"{w.name}: {w.description}", "shard_tiles": q, "shard_elems": elems,
-           "valid_elems": valid, "D": w.D, "rank": w.rank, "ms_per_step": r["ms_per_step"],
+           "valid_elems": valid, "D": w.D, "rank": w.rank, "steps": steps, "warmup": warmup,
+           "ms_per_step": r["ms_per_step"],
            "value": elems / (r["ms_per_step"] * 1e-3),
            "valid_elems_per_s": valid / (r["ms_per_step"] * 1e-3),
            "step_kernel_ms": r["kernel_ms"],
@@ -595,6 +621,8 @@ def main():
             out["pack"] = out["pack"] or p_
             out["unpack"] = out["unpack"] or u_
         out["transpose_pow2"] = time_transpose(g, r["t_next"], args.steps, stream)
+    # freed to the driver: each config below gets fresh allocations (tensors
+    # carved out of the headline's cached blocks measured up to 10% slower)
     del g
     torch.cuda.empty_cache()
     if not args.skip_configs:

@@ -186,3 +186,89 @@ def test_undersized_per_weight_tensors_are_refused():
         bfz.pack_shard(plan, grads + [grads[0]], st[0])
     torch.cuda.synchronize()
     assert not any(x.any() for x in st + d8 + dsc + dt + dts) and not codes.any()  # nothing ran
+
+
+def test_plain_call_sequence_through_the_raw_abi():
+    """The boundary's basic sequence called straight through ctypes with a
+    caller-defined six-field hyper-parameter struct (48 bytes, no options):
+    bfz_plan_create (which copies the table to the device; no
+    bfz_plan_upload call), pack_shard of master / m / v / gradient into three
+    separate tile-major arrays, adamw_fp8_step, unpack_fp8 -- bit-exact
+    with the oracle on every slot, row-major output included."""
+    import ctypes as C
+
+    import oracle
+    from synth import workloads as WL
+    from tests.compare import compare
+    from tests.oracle_run import oracle_slots
+
+    class Hyper(C.Structure):  # the caller's own copy of bfz_adamw
+        _fields_ = [("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
+                    ("eps", C.c_double), ("weight_decay", C.c_double), ("step", C.c_int64)]
+
+    assert C.sizeof(Hyper) == 48
+    w = WL.tiny()
+    _say("raw ABI sequence on", w.name, w.dims, "steps", w.steps)
+    L = C.CDLL(bfz.LIB_PATH)
+    P = C.c_void_p
+    L.bfz_plan_create.argtypes = [P, C.c_int32, C.c_int32, C.c_int32, C.POINTER(P)]
+    L.bfz_plan_shard_tiles.restype = C.c_int64
+    L.bfz_plan_shard_tiles.argtypes = [P]
+    L.bfz_plan_destroy.argtypes = [P]
+    L.bfz_plan_destroy.restype = None
+    L.pack_shard.argtypes = [P, P, P, P]
+    L.adamw_fp8_step.argtypes = [P, P, P, P, P, P, C.c_int64, C.POINTER(Hyper), P]
+    L.unpack_fp8.argtypes = [P, P, P, P, P, P]
+    L.bfz_last_error.restype = C.c_char_p
+    dims = (C.c_int64 * 3)(*w.dims[0])
+    plan = P()
+    assert L.bfz_plan_create(C.cast(dims, P), 1, w.D, w.rank, C.byref(plan)) == 0, L.bfz_last_error()
+    q = L.bfz_plan_shard_tiles(plan)
+    E, H, W = w.dims[0]
+    import synth
+    f32 = dict(dtype=torch.float32, device="cuda")
+
+    def rowmajor(tensor, step=0):
+        b = torch.empty(E * H * W, **f32)
+        synth.fill_device(w.recipe(tensor, 0, step), b, 0, E * H * W)
+        return b
+
+    stream = P(torch.cuda.current_stream().cuda_stream)
+    tiles = {k: torch.empty(q * 16384, **f32) for k in ("p", "m", "v", "g")}
+    for k, tensor in (("p", WL.MASTER), ("m", WL.MOM1), ("v", WL.MOM2)):
+        src = rowmajor(tensor)
+        arr = (P * 1)(src.data_ptr())
+        assert L.pack_shard(plan, C.cast(arr, P), P(tiles[k].data_ptr()), stream) == 0, L.bfz_last_error()
+        torch.cuda.synchronize()
+    codes = torch.empty(q * 16384, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(q, **f32)
+    for t in w.steps:
+        g = rowmajor(WL.GRAD, t)
+        arr = (P * 1)(g.data_ptr())
+        assert L.pack_shard(plan, C.cast(arr, P), P(tiles["g"].data_ptr()), stream) == 0
+        hp = Hyper(step=t, **WL.HP)
+        assert L.adamw_fp8_step(P(tiles["p"].data_ptr()), P(tiles["g"].data_ptr()), P(tiles["m"].data_ptr()),
+                                P(tiles["v"].data_ptr()), P(codes.data_ptr()), P(sc.data_ptr()), q,
+                                C.byref(hp), stream) == 0, L.bfz_last_error()
+        torch.cuda.synchronize()
+    fp8 = torch.zeros(E * H * W, dtype=torch.uint8, device="cuda")
+    grid = torch.zeros(E * -(-H // 128) * -(-W // 128), **f32)
+    a8, asc = (P * 1)(fp8.data_ptr()), (P * 1)(grid.data_ptr())
+    assert L.unpack_fp8(plan, P(codes.data_ptr()), P(sc.data_ptr()), C.cast(a8, P), C.cast(asc, P),
+                        stream) == 0, L.bfz_last_error()
+    torch.cuda.synchronize()
+    slots = list(range(q))
+    ora = oracle_slots(w, slots)
+    gpu = dict(master=tiles["p"].view(q, -1).cpu().numpy(), m=tiles["m"].view(q, -1).cpu().numpy(),
+               v=tiles["v"].view(q, -1).cpu().numpy(), codes=codes.view(q, -1).cpu().numpy(),
+               scale_inv=sc.cpu().numpy())
+    rep = compare(gpu, ora)
+    _say("raw ABI sequence:", {k: v for k, v in rep.items() if k != "fail"})
+    assert rep["ok"] and rep["exact"], rep["fail"]
+    _, _, table = oracle.plan(w.dims, w.D, w.rank)
+    o8 = np.zeros((E, H, W), dtype=np.uint8)
+    osc = np.zeros((E, -(-H // 128), -(-W // 128)), dtype=np.float32)
+    oracle.unpack(w.dims, ora["codes"].reshape(-1), ora["scale_inv"], table, [o8], [osc])
+    assert np.array_equal(fp8.cpu().numpy(), o8.reshape(-1))
+    assert np.array_equal(grid.cpu().numpy(), osc.reshape(-1))
+    L.bfz_plan_destroy(plan)
