@@ -383,7 +383,8 @@ extern "C" int bfz_transpose_pow2(const bfz_plan* plan, const uint8_t* codes,
             args.scale[k] = dst_t_scale[seg.weight0 + k];
             args.rows[k] = int32_t(plan->dims[3 * (seg.weight0 + k) + 1]);
         }
-        int err = launch_transpose_pow2(plan->d_entries + seg.slot0, seg.n_slots,
+        int err = launch_transpose_pow2(plan->d_entries + seg.slot0,
+                                        plan->d_transpose_order + seg.slot0, seg.n_slots,
                                         codes + seg.slot0 * kTileElems, scale_inv + seg.slot0,
                                         args, stream);
         if (err != hipSuccess) return hip_fail(where, err);

@@ -75,8 +75,10 @@ int launch_fold_step_unfold_t(const TileEntry* d_entries, int64_t n_slots, const
                               const UnpackArgs& outs, const TransposeArgs& touts, float* master,
                               float* m, float* v, uint8_t* codes, float* scale_inv,
                               const StepScalars& s, void* stream);
-int launch_transpose_pow2(const TileEntry* d_entries, int64_t n_slots, const uint8_t* codes,
-                          const float* scale_inv, const TransposeArgs& args, void* stream);
+// order: the launch's workgroup -> slot map (a permutation of [0, n_slots)).
+int launch_transpose_pow2(const TileEntry* d_entries, const int32_t* order, int64_t n_slots,
+                          const uint8_t* codes, const float* scale_inv, const TransposeArgs& args,
+                          void* stream);
 int launch_encode(const float* in, uint8_t* out, int64_t n, void* stream);
 const char* hip_error_string(int err);
 
@@ -92,6 +94,11 @@ struct bfz_plan {
     std::vector<int64_t> table;              // quota x {weight, e, i, j, rows, cols}
     std::vector<bfz::TileEntry> entries;     // quota rows, segment-relative `local`
     std::vector<bfz::Segment> segments;
-    bfz::TileEntry* d_entries = nullptr;     // device copy (bfz_plan_upload)
+    // The transpose's launch order: within each segment, a permutation of
+    // its slots (segment-relative) -- workgroup b of the segment's launch
+    // takes slot transpose_order[slot0 + b].  Padding slots: identity.
+    std::vector<int32_t> transpose_order;
+    bfz::TileEntry* d_entries = nullptr;     // device copy of entries, then of transpose_order
+    int32_t* d_transpose_order = nullptr;    // inside the same allocation
     int device = -1;
 };

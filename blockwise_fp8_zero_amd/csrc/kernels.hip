@@ -784,15 +784,17 @@ __device__ __forceinline__ void wt_row_full(const uint32_t v[4], int k2, int T, 
 //     LDS read) each, so a wave stores eight contiguous 128-byte row
 //     segments (wt_row: group scale, exponent edit, store).
 __global__ __launch_bounds__(kThreads) void transpose_pow2_kernel(
-    const TileEntry* __restrict__ entries, const uint8_t* __restrict__ codes,
-    const float* __restrict__ scale_inv, TransposeArgs args) {
+    const TileEntry* __restrict__ entries, const int32_t* __restrict__ order,
+    const uint8_t* __restrict__ codes, const float* __restrict__ scale_inv, TransposeArgs args) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     __shared__ uint32_t tile_t[kTileDim * 32];
-    // Plain order (workgroup b on XCD b % 8): measured 1.5-7% faster here
-    // than one contiguous eighth of the shard per XCD, and 1-7% faster than
-    // runs of 2 to 8 consecutive tiles per XCD (run_tile), on the dense and
-    // 2.01B-element shards.
-    const int64_t slot = blockIdx.x;
+    // The plan's transpose order: tile columns dealt to XCDs (see the
+    // planner).  Plain order was 1.5-7% faster than one contiguous eighth
+    // of the shard per XCD and 1-7% faster than runs of 2 to 8 consecutive
+    // tiles per XCD (run_tile) on the dense and 2.01B-element shards; the
+    // column dealing is faster still where tile rows do not hold a multiple
+    // of 8 tiles.
+    const int64_t slot = order[blockIdx.x];
     const TileEntry t = entries[slot];
     if (t.local < 0) return;
     {
@@ -1029,11 +1031,12 @@ int launch_fold_step_unfold_t(const TileEntry* d_entries, int64_t n_slots, const
     return hipGetLastError();
 }
 
-int launch_transpose_pow2(const TileEntry* d_entries, int64_t n_slots, const uint8_t* codes,
-                          const float* scale_inv, const TransposeArgs& args, void* stream) {
+int launch_transpose_pow2(const TileEntry* d_entries, const int32_t* order, int64_t n_slots,
+                          const uint8_t* codes, const float* scale_inv, const TransposeArgs& args,
+                          void* stream) {
     if (n_slots == 0) return hipSuccess;
     hipLaunchKernelGGL(transpose_pow2_kernel, dim3((uint32_t)n_slots), dim3(kThreads), 0,
-                       (hipStream_t)stream, d_entries, codes, scale_inv, args);
+                       (hipStream_t)stream, d_entries, order, codes, scale_inv, args);
     return hipGetLastError();
 }
 

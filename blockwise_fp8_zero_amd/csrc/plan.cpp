@@ -29,22 +29,29 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int build_plan(const int64_t* dims, int32_t n_weights, int32_t D, int32_t rank, int64_t total,
                bfz_plan** out);
 
-// Copies the table to the current device (the plan has no device copy yet).
+// Copies the table and the transpose order to the current device, one
+// allocation (the plan has no device copy yet).
 int upload_table(bfz_plan* plan, int dev, const char* where) {
     using namespace bfz;
-    size_t bytes = std::max<size_t>(1, plan->entries.size()) * sizeof(TileEntry);
+    const size_t n = plan->entries.size();
+    const size_t bytes = std::max<size_t>(1, n * sizeof(TileEntry) + n * sizeof(int32_t));
+    static_assert(sizeof(TileEntry) % alignof(int32_t) == 0, "order array alignment");
     TileEntry* d = nullptr;
     hipError_t err = hipMalloc(reinterpret_cast<void**>(&d), bytes);
     if (err != hipSuccess) return fail(BFZ_EHIP, "%s: hipMalloc: %s", where, hipGetErrorString(err));
-    if (!plan->entries.empty()) {
-        err = hipMemcpy(d, plan->entries.data(), plan->entries.size() * sizeof(TileEntry),
-                        hipMemcpyHostToDevice);
+    int32_t* d_order = reinterpret_cast<int32_t*>(d + n);
+    if (n) {
+        err = hipMemcpy(d, plan->entries.data(), n * sizeof(TileEntry), hipMemcpyHostToDevice);
+        if (err == hipSuccess)
+            err = hipMemcpy(d_order, plan->transpose_order.data(), n * sizeof(int32_t),
+                            hipMemcpyHostToDevice);
         if (err != hipSuccess) {
             (void)hipFree(d);
             return fail(BFZ_EHIP, "%s: hipMemcpy: %s", where, hipGetErrorString(err));
         }
     }
     plan->d_entries = d;
+    plan->d_transpose_order = d_order;
     plan->device = dev;
     return BFZ_OK;
 }
@@ -74,7 +81,7 @@ extern "C" int bfz_plan_create(const int64_t* dims, int32_t n_weights, int32_t D
         total += E * grid;
     }
     // A shard beyond 2^31 - 1 tiles (3.5e13 elements) is far past any one
-    // GPU's memory; refusing it keeps the host table (76 B per slot) sane.
+    // GPU's memory; refusing it keeps the host table (80 B per slot) sane.
     if (ceil_div(total, D) > int64_t(INT32_MAX))
         return fail(BFZ_EINVAL, "bfz_plan_create: %lld tiles over %d ranks is more than 2^31 - 1 per rank",
                     (long long)total, D);
@@ -101,6 +108,58 @@ extern "C" int bfz_plan_create(const int64_t* dims, int32_t n_weights, int32_t D
 }
 
 namespace {
+
+// The transpose's launch order.  The dispatcher deals workgroups to the 8
+// XCDs round-robin (b on XCD b % 8), and the tiles of one tile column write
+// neighbouring pieces of the same W^T rows and group-scale rows, so each
+// segment's slots are dealt to XCDs by tile column: queue x holds the slots
+// with j % 8 == x, and position 8 k + x of the order takes the k-th slot of
+// queue x (the queues' remainders, beyond the shortest, follow in slot
+// order).  Inside a queue the slots stay in fold order (along tile rows),
+// except for weights whose tile rows hold a number of tiles that is not a
+// multiple of 8, which go down their tile columns (column-major).  With 8 |
+// tiles per row, plain order already deals by column; the order changes
+// the other weights.  Measured against plain order (one process, one box):
+// dense-LLM shard 0.3135 -> 0.3003 ms, ragged 0.0459 -> 0.0405 ms, the
+// 4096x4096 and MoE shards unchanged; going down the columns for every
+// weight was 2.5% slower on the 4096x4096 shard.
+void build_transpose_order(bfz_plan* plan) {
+    using namespace bfz;
+    const int64_t q = plan->quota;
+    plan->transpose_order.resize(size_t(q));
+    for (const Segment& seg : plan->segments) {
+        int32_t* ord = plan->transpose_order.data() + seg.slot0;
+        const int32_t n = int32_t(seg.n_slots);
+        if (seg.n_weights == 0) {  // padding: never launched
+            for (int32_t r = 0; r < n; ++r) ord[r] = r;
+            continue;
+        }
+        const int64_t* row = &plan->table[size_t(6 * seg.slot0)];
+        std::vector<int32_t> queue[8];
+        for (int32_t r = 0; r < n; ++r) queue[row[6 * r + 3] % 8].push_back(r);
+        for (auto& qx : queue) {
+            std::stable_sort(qx.begin(), qx.end(), [&](int32_t a, int32_t b) {
+                const int64_t* ta = row + 6 * a;
+                const int64_t* tb = row + 6 * b;
+                if (ta[0] != tb[0]) return ta[0] < tb[0];  // weight
+                if (ta[1] != tb[1]) return ta[1] < tb[1];  // expert
+                const int64_t W = plan->dims[size_t(3 * ta[0] + 2)];
+                if ((W + kTileDim - 1) / kTileDim % 8 == 0) return false;  // fold order kept
+                if (ta[3] != tb[3]) return ta[3] < tb[3];  // column-major: j, then i
+                return ta[2] < tb[2];
+            });
+        }
+        size_t shortest = queue[0].size();
+        for (const auto& qx : queue) shortest = std::min(shortest, qx.size());
+        int32_t pos = 0;
+        for (size_t k = 0; k < shortest; ++k)
+            for (const auto& qx : queue) ord[pos++] = qx[k];
+        std::vector<int32_t> rest;
+        for (const auto& qx : queue) rest.insert(rest.end(), qx.begin() + ptrdiff_t(shortest), qx.end());
+        std::sort(rest.begin(), rest.end());
+        for (int32_t r : rest) ord[pos++] = r;
+    }
+}
 
 int build_plan(const int64_t* dims, int32_t n_weights, int32_t D, int32_t rank, int64_t total,
                bfz_plan** out) {
@@ -166,6 +225,7 @@ int build_plan(const int64_t* dims, int32_t n_weights, int32_t D, int32_t rank, 
     if (plan->owned < q) {  // padding slots ride in a segment of their own
         plan->segments.push_back(Segment{plan->owned, q - plan->owned, 0, 0});
     }
+    build_transpose_order(plan.get());
     *out = plan.release();
     return BFZ_OK;
 }

@@ -110,7 +110,7 @@ typedef struct {
  * the largest one; the contiguous equal quota is this library's reading of
  * how the page deals tiles to ranks).
  * The table is built on the host and, when the process sees a HIP device,
- * copied to the current device (about 24 bytes per tile, allocated here and
+ * copied to the current device (about 28 bytes per tile, allocated here and
  * freed by bfz_plan_destroy; synchronous).  Every call that takes the plan
  * then needs that device to be current.  On a host with no HIP device the
  * plan is host-only: the queries below work, the device calls return
@@ -118,7 +118,7 @@ typedef struct {
  * On success *out receives a new plan.  Errors: BFZ_EINVAL for null
  * pointers, n_params < 1, D < 1, rank outside [0, D), a dimension < 1,
  * H, W > 2^31 - 1, a weight of more than 2^31 - 1 tiles, a quota q of more
- * than 2^31 - 1 tiles, or too little host memory for the table (76 bytes
+ * than 2^31 - 1 tiles, or too little host memory for the table (80 bytes
  * per slot); BFZ_EHIP if the device copy fails.
  */
 int bfz_plan_create(const int64_t* dims, int32_t n_params, int32_t D, int32_t rank,

@@ -219,10 +219,20 @@ int launch_fold_step_unfold_t(const TileEntry* e, int64_t n, const PackArgs& gra
     return 0;
 }
 
-int launch_transpose_pow2(const TileEntry* e, int64_t n, const uint8_t* codes,
+int launch_transpose_pow2(const TileEntry* e, const int32_t* order, int64_t n, const uint8_t* codes,
                           const float* scale_inv, const TransposeArgs& args, void*) {
     if (int err = record(e, n)) return err;
-    for (int64_t s = 0; s < n; ++s) {
+    // the launch order must be a permutation of the segment's slots: each
+    // workgroup takes one slot, every slot once
+    std::vector<char> seen(size_t(n), 0);
+    for (int64_t b = 0; b < n; ++b) {
+        CHECK(order[b] >= 0 && order[b] < n && !seen[size_t(order[b])],
+              "transpose order: workgroup %lld takes slot %d of %lld", (long long)b, order[b], (long long)n);
+        if (order[b] >= 0 && order[b] < n) seen[size_t(order[b])] = 1;
+    }
+    for (int64_t b = 0; b < n; ++b) {
+        const int64_t s = order[b];
+        if (s < 0 || s >= n) continue;
         const TileEntry& t = e[s];
         if (t.local < 0) continue;
         const int64_t H = args.rows[t.local], W = t.ld;
@@ -745,6 +755,9 @@ int main() {
     // tile-row counts that are not multiples of 4
     run_plan_case({1, 1100, 300, 2, 700, 520}, 3);
     run_plan_case({1, 2000, 130, 1, 129, 4000}, 5);
+    // tile rows of 8 and 16 tiles (kept in fold order by the transpose's
+    // launch order) beside rows of 3 and 11 (dealt down their columns)
+    run_plan_case({1, 300, 1024, 2, 260, 2048, 1, 500, 300, 1, 200, 1400}, 2);
     // both state layouts, one weight and several segments
     run_layout_case({2, 300, 200, 1, 129, 257}, 2);
     run_layout_case(many, 3);
