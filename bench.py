@@ -322,9 +322,10 @@ def sampled_gpu_slots(g, n_random=24):
 
 
 def oracle_leg(w, gpu_sample, tiny_gpu):
-    """The oracle's side of the run (the only part of bench.py that loads
-    it): parity counts of the sampled headline slots and of the tiny
-    workload, and the CPU baseline."""
+    """Parity counts of the sampled headline slots and of the tiny workload
+    against the oracle.  With cpu_baseline below, this is the CPU-baseline
+    leg of the run, the only part of bench.py that loads the oracle (both
+    are skipped by --skip-cpu-baseline)."""
     import numpy as np
 
     import oracle
