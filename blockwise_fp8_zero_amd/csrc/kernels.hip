@@ -8,6 +8,7 @@
 // HIP defaults), so results do not depend on instruction scheduling.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 
@@ -18,7 +19,8 @@
 namespace bfz {
 namespace {
 
-constexpr int kThreads = 256;  // unfold / encode: 4 wave64s per workgroup
+constexpr int kThreads = 256;  // transpose / encode: 4 wave64s per workgroup
+constexpr int kUnpackThreads = 1024;  // unfold: one 16-byte piece per thread
 
 // ---------------------------------------------------------------------
 // E4M3 (OCP E4M3FN) rounding of a binary32 value: nearest value, ties to
@@ -142,11 +144,16 @@ __device__ __forceinline__ uint32_t pack_codes(const f32x4& x, float scale) {
 //   step kernels, R = 4: one-kernel step 2.01B-element shard 9.75 -> 9.58 ms,
 //     dense 3.92 -> 3.88, MoE 1.71 -> 1.69, ragged 0.366 -> 0.359 (R = 2
 //     within 0.5% of 4; 8 and 16 slower);
-//   fold (pack_kernel), R = 2: dense 1.034 -> 1.023 ms, 2.01B 2.527 -> 2.477,
-//     ragged unchanged (longer runs up to 2% slower on the large shards);
-//   unfold (unpack_kernel), R = 32 (a whole tile row of a 4096-wide weight
-//     per XCD): dense 0.280 -> 0.268 ms, 2.01B 0.688 -> 0.657, ragged
-//     0.0468 -> 0.0451 (R = 2..16 in between, 64 slightly slower).
+//   fold (pack_kernel, whole-tile workgroups at the time), R = 2: dense
+//     1.034 -> 1.023 ms, 2.01B 2.527 -> 2.477, ragged unchanged (longer
+//     runs up to 2% slower on the large shards); with quarter-tile
+//     workgroups the unit is a quarter tile and R = 64 (16 tiles; 8 to
+//     32 tiles within 1.5%, 1 and 2 tiles 5-10% slower);
+//   unfold (unpack_kernel, 256-thread workgroups at the time), R = 32 (a
+//     whole tile row of a 4096-wide weight per XCD): dense 0.280 -> 0.268
+//     ms, 2.01B 0.688 -> 0.657, ragged 0.0468 -> 0.0451 (R = 2..16 in
+//     between, 64 slightly slower); the 1024-thread form keeps R = 32
+//     (8 to 64 within 1%).
 // The transpose keeps plain order (below).
 template <int64_t R>
 __device__ __forceinline__ int64_t run_tile(int64_t b, int64_t n_tiles) {
@@ -155,7 +162,7 @@ __device__ __forceinline__ int64_t run_tile(int64_t b, int64_t n_tiles) {
     const int64_t x = b % 8, j = b / 8;
     return (j / R) * (8 * R) + x * R + j % R;
 }
-constexpr int64_t kStepRun = 4, kPackRun = 2, kUnpackRun = 32;
+constexpr int64_t kStepRun = 4, kPackRun = 64, kUnpackRun = 32;
 __device__ __forceinline__ int64_t step_tile_of(int64_t b, int64_t n_tiles) {
     return run_tile<kStepRun>(b, n_tiles);
 }
@@ -463,38 +470,44 @@ __global__ __launch_bounds__(kStepThreads) void fold_step_unfold_kernel(
     });
 }
 
-// Fold: one 1024-thread workgroup per slot, the step kernels' thread
-// layout: thread t moves float4 column t % 32 of rows t / 32 + 32 k, k < 4,
-// so a wave covers two 512-byte tile rows per instruction on both sides.
-// All four loads are issued before the stores; streaming loads, and the
-// block's stores at device scope as in the step kernels.  Outside
-// the weight's edge, and in padding slots, the tile gets +0.0.  Slot s is
-// written at dst + s * dst_stride.
+// Fold: one 1024-thread workgroup per quarter slot.  Unit u covers float4
+// group k = u % 4 of slot u / 4 in the step kernels' thread layout: thread t
+// moves float4 column t % 32 of row 32 k + t / 32, so a wave covers two
+// 512-byte tile rows per instruction on both sides.  Units run in runs of
+// 64 (16 tiles) per XCD.  Whole-tile workgroups (four float4 per thread, all
+// loaded before the stores) hold four times the bytes in flight per
+// workgroup and measured 3-7% slower: dense shard 1.023 -> 0.992 ms,
+// 2.01B-element shard 2.485 -> 2.397, MoE 0.448 -> 0.420, ragged 0.099 ->
+// 0.094 (one process, five repeats; half-tile units in between).
+// Streaming loads, and the block's stores at device scope as in the step
+// kernels.  Outside the weight's edge, and in padding slots, the tile gets
+// +0.0.  Slot s is written at dst + s * dst_stride.
 __global__ __launch_bounds__(kStepThreads) void pack_kernel(const TileEntry* __restrict__ entries,
                                                             float* __restrict__ dst, int64_t dst_stride,
                                                             PackArgs args) {
-    const int64_t slot = run_tile<kPackRun>(blockIdx.x, gridDim.x);
+    const int64_t u = run_tile<kPackRun>(blockIdx.x, gridDim.x);
+    const int64_t slot = u / kStepVec;
+    const int k = (int)(u % kStepVec);
     const TileEntry t = entries[slot];
     f32x4* out = reinterpret_cast<f32x4*>(dst + slot * dst_stride);
     const TileBlock block(out, kTileElems * 4);
-    // a lane with nothing to read loads its own (not yet written) output block
+    const int i = k * kStepThreads + threadIdx.x;
+    // a lane with nothing to read loads its own (not yet written) output float4
     with_row_major_grad(t, args, [&](const auto& src) {
-        typename std::decay_t<decltype(src)>::Raw raw[kStepVec];
-#pragma unroll
-        for (int k = 0; k < kStepVec; ++k) raw[k] = src.load(k, out + k * kStepThreads + threadIdx.x);
-        f32x4 x[kStepVec];
-#pragma unroll
-        for (int k = 0; k < kStepVec; ++k) x[k] = src.finish(k, raw[k]);
-#pragma unroll
-        for (int k = 0; k < kStepVec; ++k) block.store(k * kStepThreads + threadIdx.x, x[k]);
+        const auto raw = src.load(k, out + i);
+        block.store(i, src.finish(k, raw));
     });
 }
 
-// Unfold of codes and scales: one workgroup per owned slot, in runs of 32
-// tiles per XCD (run_tile; plain order measured 5.6% slower on the dense
-// shard than one contiguous eighth per XCD, itself 4% slower than this).  Thread t moves
-// 16 codes (column block t % 8) of rows t / 8, t / 8 + 32, ...  A row of a
-// full-width tile goes out as one 16-byte store per lane when it starts on a
+// Unfold of codes and scales: one 1024-thread workgroup per owned slot, in
+// runs of 32 tiles per XCD (run_tile; plain order measured 5.6% slower on
+// the dense shard than one contiguous eighth per XCD, itself 4% slower than
+// this).  Thread t moves one 16-byte piece: the 16 codes of column block
+// t % 8 in row t / 8.  (A 256-thread workgroup moving four pieces per
+// thread, all loaded before the first store, holds more bytes in flight per
+// CU and measured 4-7% slower on full tiles of 4096- and 11008-wide
+// weights; so did two or four tiles per workgroup.)  A row of a full-width
+// tile goes out as one 16-byte store per lane when it starts on a
 // 16-byte boundary, as 4-byte words when on a 4-byte boundary, and otherwise
 // as aligned words built from the lane's codes and its left neighbour's last
 // word (a shuffle within the row's 8 lanes), with bytes only for the row's
@@ -502,10 +515,9 @@ __global__ __launch_bounds__(kStepThreads) void pack_kernel(const TileEntry* __r
 // row shares its end cache lines with the neighbouring tiles, and the L2
 // merges the halves (streaming stores of partial lines measured about 1.6x
 // slower).  Ragged-width tiles use the widest store each lane's piece allows.
-__global__ __launch_bounds__(kThreads) void unpack_kernel(const TileEntry* __restrict__ entries,
-                                                          const uint8_t* __restrict__ codes,
-                                                          const float* __restrict__ scale_inv,
-                                                          UnpackArgs args) {
+__global__ __launch_bounds__(kUnpackThreads) void unpack_kernel(
+    const TileEntry* __restrict__ entries, const uint8_t* __restrict__ codes,
+    const float* __restrict__ scale_inv, UnpackArgs args) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const int64_t slot = run_tile<kUnpackRun>(blockIdx.x, gridDim.x);
     const TileEntry t = entries[slot];
@@ -513,19 +525,12 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const TileEntry* __res
     const u32x4* in = reinterpret_cast<const u32x4*>(codes + slot * kTileElems);
     uint8_t* dst = args.codes[t.local] + t.base;
     const int c16 = threadIdx.x & 7;
-    const int r0 = threadIdx.x >> 3;
+    const int r = threadIdx.x >> 3;
     const int col = 16 * c16;
     const bool full = t.valid_cols == kTileDim;
-    // all four row pieces are loaded before any store (the tile always holds
-    // 128 rows, padding included, so every load is in bounds)
-    u32x4 xs[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) xs[k] = __builtin_nontemporal_load(in + (r0 + 32 * k) * 8 + c16);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int r = r0 + 32 * k;
-        if (r >= t.valid_rows) break;  // the same for the 8 lanes of a row
-        const u32x4 x = xs[k];
+    // the tile always holds 128 rows (padding included), so the load is in bounds
+    const u32x4 x = __builtin_nontemporal_load(in + r * 8 + c16);
+    if (r < t.valid_rows) {  // the same for the 8 lanes of a row
         const uint32_t o[4] = {x[0], x[1], x[2], x[3]};
         uint8_t* row = dst + (int64_t)r * t.ld + col;
         const uintptr_t seg = reinterpret_cast<uintptr_t>(row) - (uintptr_t)col;
@@ -1003,16 +1008,23 @@ int launch_fold_step_unfold(const TileEntry* d_entries, int64_t n_slots, const P
 
 int launch_pack(const TileEntry* d_entries, int64_t n_slots, float* dst, int64_t dst_stride,
                 const PackArgs& args, void* stream) {
-    if (n_slots == 0) return hipSuccess;
-    hipLaunchKernelGGL(pack_kernel, dim3((uint32_t)n_slots), dim3(kStepThreads), 0,
-                       (hipStream_t)stream, d_entries, dst, dst_stride, args);
-    return hipGetLastError();
+    // four workgroups per slot: at most 2^28 slots (2^30 workgroups) a launch
+    constexpr int64_t kMaxSlots = int64_t(1) << 28;
+    for (int64_t s0 = 0; s0 < n_slots; s0 += kMaxSlots) {
+        const int64_t n = std::min(kMaxSlots, n_slots - s0);
+        hipLaunchKernelGGL(pack_kernel, dim3((uint32_t)(kStepVec * n)), dim3(kStepThreads), 0,
+                           (hipStream_t)stream, d_entries + s0, dst + s0 * dst_stride, dst_stride,
+                           args);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
 }
 
 int launch_unpack(const TileEntry* d_entries, int64_t n_slots, const uint8_t* codes,
                   const float* scale_inv, const UnpackArgs& args, void* stream) {
     if (n_slots == 0) return hipSuccess;
-    hipLaunchKernelGGL(unpack_kernel, dim3((uint32_t)n_slots), dim3(kThreads), 0,
+    hipLaunchKernelGGL(unpack_kernel, dim3((uint32_t)n_slots), dim3(kUnpackThreads), 0,
                        (hipStream_t)stream, d_entries, codes, scale_inv, args);
     return hipGetLastError();
 }
