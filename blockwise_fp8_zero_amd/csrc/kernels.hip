@@ -1008,8 +1008,9 @@ int launch_fold_step_unfold(const TileEntry* d_entries, int64_t n_slots, const P
 
 int launch_pack(const TileEntry* d_entries, int64_t n_slots, float* dst, int64_t dst_stride,
                 const PackArgs& args, void* stream) {
-    // four workgroups per slot: at most 2^28 slots (2^30 workgroups) a launch
-    constexpr int64_t kMaxSlots = int64_t(1) << 28;
+    // four 1024-thread workgroups per slot, and a launch counts its
+    // work-items in 32 bits: at most 2^20 - 1 slots a launch
+    constexpr int64_t kMaxSlots = (int64_t(1) << 32) / (kStepVec * kStepThreads) - 1;
     for (int64_t s0 = 0; s0 < n_slots; s0 += kMaxSlots) {
         const int64_t n = std::min(kMaxSlots, n_slots - s0);
         hipLaunchKernelGGL(pack_kernel, dim3((uint32_t)(kStepVec * n)), dim3(kStepThreads), 0,

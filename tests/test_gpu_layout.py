@@ -73,6 +73,39 @@ def test_pack_offset_bases(off):
     assert np.array_equal(dst.cpu().numpy().view(np.uint32), want.view(np.uint32))
 
 
+def test_pack_segment_beyond_32bit_work_items():
+    """One weight of 1024 x 1025 tiles (1,049,600 slots, 17.2G elements,
+    69 GB a side): the fold runs four 1024-thread workgroups per slot, so
+    this launch segment holds more work-items than one launch can count in
+    32 bits and goes out in two launches.  Every tile must hold its block of
+    the weight, bit for bit.  The fold is a pure layout copy, so the
+    weight's own blocks are the reference; the values name their position
+    (row-major index mod 2^24, exact in float32)."""
+    H, W = 128 * 1024, 128 * 1025
+    hb, wb = H // 128, W // 128
+    plan = bfz.Plan([(1, H, W)], 1, 0)
+    q = plan.shard_tiles
+    assert q == hb * wb and q * 4 * 1024 >= 2 ** 32
+    _say("pack of one", H, "x", W, "weight:", q, "slots in one segment")
+    src = torch.empty(H * W, dtype=torch.float32, device="cuda")
+    cols = torch.arange(W, dtype=torch.int64, device="cuda")
+    for r0 in range(0, H, 1024):
+        rows = torch.arange(r0, r0 + 1024, dtype=torch.int64, device="cuda")
+        src.view(H, W)[r0:r0 + 1024] = ((rows[:, None] * W + cols[None, :]) % (1 << 24)).float()
+    del cols, rows
+    dst = torch.full((q * 16384,), float("nan"), dtype=torch.float32, device="cuda")
+    bfz.pack_shard(plan, [src], dst)
+    torch.cuda.synchronize()
+    tiles = dst.view(hb, wb, 128, 128)
+    blocks = src.view(hb, 128, wb, 128)
+    for i0 in range(0, hb, 64):
+        ok = torch.equal(tiles[i0:i0 + 64].view(torch.int32),
+                         blocks[i0:i0 + 64].permute(0, 2, 1, 3).view(torch.int32))
+        assert ok, ("tile rows", i0, i0 + 63)
+    del tiles, blocks, src, dst
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("case", range(len(CASES)))
 def test_unpack_matches_oracle(case):
     dims, D, rank = CASES[case]
