@@ -96,8 +96,20 @@ __host__ __device__ inline double ln_pos(double x) {
     return (double)e * kLn2 + 2.0 * s * poly;
 }
 
-// 1/n!, folded at compile time (identically on host and device).
-constexpr double inv_fact(int n) { return n <= 1 ? 1.0 : inv_fact(n - 1) / (double)n; }
+// 1/n! for n = 0..22: 1/n! = (1/(n-1)!) / n, one correctly rounded division
+// per step, evaluated once at compile time into a table (a recursive
+// constexpr call in a plain expression is not guaranteed to fold, and the
+// host build did evaluate it at run time, ~20 divisions per use).
+struct InvFactTable {
+    double v[23];
+    constexpr InvFactTable() : v() {
+        v[0] = 1.0;
+        v[1] = 1.0;
+        for (int n = 2; n < 23; ++n) v[n] = v[n - 1] / (double)n;
+    }
+};
+constexpr InvFactTable kInvFact{};
+__host__ __device__ constexpr double inv_fact(int n) { return kInvFact.v[n]; }
 
 // exp x for |x| < 700: x = k ln2 + r, |r| <= ln2/2, Taylor series of e^r
 // (Horner form, degree 22).
@@ -154,15 +166,15 @@ __host__ __device__ inline double student_t3(uint64_t key, uint64_t j) {
     return z0 / sqrt_pos(chi);
 }
 
-__host__ __device__ inline float value_at(const synth_recipe& r, int64_t k) {
-    int64_t per_expert = r.H * r.W;
-    if (r.zero_tile_prob > 0.0) {
-        int64_t e = k / per_expert, rem = k - e * per_expert;
-        int64_t row = rem / r.W, col = rem - row * r.W;
-        int64_t wb = (r.W + 127) / 128, hb = (r.H + 127) / 128;
-        int64_t tile = (e * hb + row / 128) * wb + col / 128;
-        if (uniform(r.zero_key, (uint64_t)tile) < r.zero_tile_prob) return 0.0f;
-    }
+// Whether the 128x128 tile (e, ti, tj) of the tensor is drawn all zero.
+__host__ __device__ inline bool zero_tile(const synth_recipe& r, int64_t e, int64_t ti, int64_t tj) {
+    const int64_t wb = (r.W + 127) / 128, hb = (r.H + 127) / 128;
+    return uniform(r.zero_key, (uint64_t)((e * hb + ti) * wb + tj)) < r.zero_tile_prob;
+}
+
+// Value k ignoring the zero tiles.
+__host__ __device__ inline float value_raw(const synth_recipe& r, int64_t k) {
+    const int64_t per_expert = r.H * r.W;
     double v;
     switch (r.kind) {
         case SYNTH_NORMAL: v = r.scale * normal(r.key, (uint64_t)k); break;
@@ -182,6 +194,16 @@ __host__ __device__ inline float value_at(const synth_recipe& r, int64_t k) {
         default: v = 0.0; break;
     }
     return (float)v;
+}
+
+__host__ __device__ inline float value_at(const synth_recipe& r, int64_t k) {
+    if (r.zero_tile_prob > 0.0) {
+        const int64_t per_expert = r.H * r.W;
+        const int64_t e = k / per_expert, rem = k - e * per_expert;
+        const int64_t row = rem / r.W, col = rem - row * r.W;
+        if (zero_tile(r, e, row / 128, col / 128)) return 0.0f;
+    }
+    return value_raw(r, k);
 }
 
 __global__ void fill_kernel(float* __restrict__ out, int64_t lo, int64_t n, synth_recipe r) {
@@ -224,6 +246,17 @@ int synth_fill_rect_host(float* out, int64_t e, int64_t r0, int64_t nr, int64_t 
     if (!out || !r || e < 0 || r0 < 0 || c0 < 0 || nr < 0 || nc < 0 || r0 + nr > r->H ||
         c0 + nc > r->W)
         return -1;
+    // a rectangle inside one tile (the oracle's per-slot draws) decides the
+    // tile's zero draw once
+    const bool one_tile = nr > 0 && nc > 0 && r0 / 128 == (r0 + nr - 1) / 128 &&
+                          c0 / 128 == (c0 + nc - 1) / 128;
+    if (one_tile && r->zero_tile_prob > 0.0) {
+        const bool zero = zero_tile(*r, e, r0 / 128, c0 / 128);
+        for (int64_t a = 0; a < nr; ++a)
+            for (int64_t b = 0; b < nc; ++b)
+                out[a * nc + b] = zero ? 0.0f : value_raw(*r, (e * r->H + r0 + a) * r->W + c0 + b);
+        return 0;
+    }
     for (int64_t a = 0; a < nr; ++a)
         for (int64_t b = 0; b < nc; ++b)
             out[a * nc + b] = value_at(*r, (e * r->H + r0 + a) * r->W + c0 + b);
