@@ -622,7 +622,7 @@ def main():
             out["pack"] = out["pack"] or p_
             out["unpack"] = out["unpack"] or u_
         out["transpose_pow2"] = time_transpose(g, r["t_next"], args.steps, stream)
-    # freed to the driver: each config below gets fresh allocations (tensors
+    # memory returned to the HIP runtime: each config below gets fresh allocations (tensors
     # carved out of the headline's cached blocks measured up to 10% slower)
     del g
     torch.cuda.empty_cache()
