@@ -14,8 +14,8 @@ grid.  --path picks how:
 The split itself (the planner) runs once at set-up.
 --layout picks how the FP32 state (master, m, v) sits in HBM:
   interleaved (default): one contiguous [master | m | v] block per tile
-      (state_stride 49152), so each tile's updated state leaves as one
-      write stream;
+      and a 4 KiB gap (state_stride 50176), so each tile's updated state
+      leaves as one write stream;
   separate: three tile-major arrays.
 
 Default workload (the headline): the large shard -- 120 matrices of
@@ -578,7 +578,7 @@ def main():
             "rank": w.rank,
             "first_timed_step_t": first["t_next"] + args.warmup,
             "state_layout": {"interleaved": "one [master | m | v] block per tile "
-                                            "(state_stride 49152)",
+                                            "and a 4 KiB gap (state_stride 50176)",
                              "separate": "three tile-major arrays"}[args.layout],
             "step_path": {"unfused": "pack_shard(grad) + adamw_fp8_step + unpack_fp8",
                           "fused": "fold_adamw_fp8_step + unpack_fp8",

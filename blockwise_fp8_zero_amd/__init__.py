@@ -15,10 +15,10 @@ LIB_PATH = os.path.join(HERE, "libbfz.so")
 TILE = 128
 TILE_ELEMS = TILE * TILE
 # the interleaved state layout (BFZ_STATE_STRIDE_INTERLEAVED): one
-# [master | m | v] block per tile; with state = torch.zeros(q, STATE_STRIDE),
-# pass state[:, :16384], state[:, 16384:32768] and state[:, 32768:] as
-# master, m and v
-STATE_STRIDE = 49152
+# [master | m | v] block per tile and a 4 KiB gap; with
+# state = torch.zeros(q, STATE_STRIDE), pass state[:, :16384],
+# state[:, 16384:32768] and state[:, 32768:49152] as master, m and v
+STATE_STRIDE = 50176
 
 BFZ_OK, BFZ_EINVAL, BFZ_EALIGN, BFZ_EHIP, BFZ_ESTATE = 0, -1, -2, -3, -4
 

@@ -233,7 +233,7 @@ _BIG = {}
 
 
 # each route once; the one-kernel step in the interleaved layout, whose
-# state offsets (slot * 49152 floats) pass 2^32 already at slot 87,382
+# state offsets (slot * 50176 floats) pass 2^32 already at slot 85,599
 @pytest.mark.parametrize("mode,layout", [("unfused", "separate"), ("fused", "separate"),
                                          ("fused_unpack", "interleaved")])
 def test_offsets_beyond_32_bits(mode, layout):
