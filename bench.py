@@ -501,6 +501,20 @@ def config_line(w, args, stream):
     return out
 
 
+def device_info():
+    """The GPU the line was measured on (boxes of one model differ by a few
+    percent in these numbers): name, architecture, CUs, memory, and the
+    device's PCI bus id so that runs on one board can be told apart."""
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count, "memory_GiB": round(p.total_memory / 2 ** 30, 1)}
+    for key in ("pci_bus_id", "pci_device_id", "pci_domain_id"):
+        if hasattr(p, key):
+            info[key] = getattr(p, key)
+    return info
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -611,6 +625,7 @@ def main():
         "unpack": None,
         "transpose_pow2": None,
         "configs": None,
+        "device": device_info(),
     }
     if r["pack_ms"] is not None:
         out["pack"] = pass_stats(r["pack_ms"], 4 * valid + 4 * elems)

@@ -45,5 +45,7 @@ def test_bench_prints_the_contract_line():
     par = b["parity"]
     assert par["headline"]["bit_exact"] and par["headline"]["code_mismatches"] == 0
     assert par["tiny"]["bit_exact"]
+    dev = b["device"]
+    assert dev["compute_units"] == 256 and "gfx950" in (dev["arch"] or ""), dev
     cb = b["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
